@@ -1,0 +1,188 @@
+"""ctypes front end of the C oracle (tcq_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Argument marshalling lives here; every number is computed
+by the C code, which follows the pages' definitions step by step (see the header of
+tcq_oracle.c for the passages and the fp32 evaluation order).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tcq_oracle.c")
+_LIB = os.path.join(_HERE, "libtcq_oracle.so")
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    lib.oracle_inv_normal_cdf.restype = ctypes.c_double
+    lib.oracle_inv_normal_cdf.argtypes = [ctypes.c_double]
+    lib.oracle_splitmix64_next.restype = ctypes.c_uint64
+    lib.oracle_splitmix64_next.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
+    lib.oracle_make_codebook.restype = ctypes.c_int
+    lib.oracle_make_codebook.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint64, _f32p]
+    lib.oracle_encode_block.restype = ctypes.c_int
+    lib.oracle_encode_block.argtypes = [_f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, _u32p,
+                                        _u32p, _f32p]
+    lib.oracle_two_best_block.restype = ctypes.c_int
+    lib.oracle_two_best_block.argtypes = [_f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, _f32p,
+                                          _f32p]
+    lib.oracle_decode_block.restype = None
+    lib.oracle_decode_block.argtypes = [_u32p, ctypes.c_uint32, _f32p, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, _f32p]
+    lib.oracle_path_cost.restype = ctypes.c_float
+    lib.oracle_path_cost.argtypes = [_f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, _u32p, ctypes.c_uint32]
+    _lib = lib
+    return lib
+
+
+def _fp(a):
+    return None if a is None else a.ctypes.data_as(_f32p)
+
+
+def _up(a):
+    return a.ctypes.data_as(_u32p)
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def nwords(k: int, T: int) -> int:
+    return (k * T + 31) // 32
+
+
+def inv_normal_cdf(p: float) -> float:
+    return _load().oracle_inv_normal_cdf(float(p))
+
+
+def splitmix64_stream(seed: int, count: int) -> list[int]:
+    st = ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF)
+    lib = _load()
+    return [lib.oracle_splitmix64_next(ctypes.byref(st)) for _ in range(count)]
+
+
+def make_codebook(L: int, V: int, seed: int) -> np.ndarray:
+    out = np.empty((1 << L, V), dtype=np.float32)
+    rc = _load().oracle_make_codebook(L, V, seed, _fp(out))
+    if rc != 0:
+        raise ValueError(f"oracle_make_codebook failed ({rc})")
+    return out
+
+
+def encode_block(w, d, C, L, k, V, T, fixed_s0=-1):
+    """Returns (bits uint32[nwords], s0, cost)."""
+    w = _f32(w)
+    d = _f32(d)
+    C = _f32(C)
+    assert w.size == T and (d is None or d.size == T) and C.size == (1 << L) * V
+    bits = np.zeros(nwords(k, T), dtype=np.uint32)
+    s0 = ctypes.c_uint32(0)
+    cost = ctypes.c_float(0)
+    rc = _load().oracle_encode_block(_fp(w), _fp(d), _fp(C), L, k, V, T, fixed_s0,
+                                     _up(bits), ctypes.byref(s0), ctypes.byref(cost))
+    if rc != 0:
+        raise ValueError(f"oracle_encode_block failed ({rc})")
+    return bits, int(s0.value), np.float32(cost.value)
+
+
+def two_best_block(w, d, C, L, k, V, T, fixed_s0=-1):
+    w = _f32(w)
+    d = _f32(d)
+    C = _f32(C)
+    best = ctypes.c_float(0)
+    second = ctypes.c_float(0)
+    rc = _load().oracle_two_best_block(_fp(w), _fp(d), _fp(C), L, k, V, T, fixed_s0,
+                                       ctypes.byref(best), ctypes.byref(second))
+    if rc != 0:
+        raise ValueError(f"oracle_two_best_block failed ({rc})")
+    return np.float32(best.value), np.float32(second.value)
+
+
+def decode_block(bits, s0, C, L, k, V, T):
+    bits = np.ascontiguousarray(bits, dtype=np.uint32)
+    C = _f32(C)
+    out = np.empty(T, dtype=np.float32)
+    _load().oracle_decode_block(_up(bits), s0, _fp(C), L, k, V, T, _fp(out))
+    return out
+
+
+def path_cost(w, d, C, L, k, V, T, bits, s0):
+    w = _f32(w)
+    d = _f32(d)
+    C = _f32(C)
+    bits = np.ascontiguousarray(bits, dtype=np.uint32)
+    return np.float32(_load().oracle_path_cost(_fp(w), _fp(d), _fp(C), L, k, V, T,
+                                                _up(bits), s0))
+
+
+def encode_matrix(W, d, C, L, k, V, T, blocks=None, threads=1):
+    """Encode coding blocks of a row-major M x N matrix.
+
+    Block b = r * (N // T) + c covers W[r, c*T:(c+1)*T] and d[c*T:(c+1)*T].
+    `blocks` selects a subset (default: all).  Blocks are independent; `threads` > 1
+    runs whole blocks on a thread pool (each block is still single-threaded).
+    Returns (bits [nb, nwords], s0 [nb], cost [nb]) for the selected blocks.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    M, N = W.shape
+    assert N % T == 0
+    per_row = N // T
+    if blocks is None:
+        blocks = np.arange(M * per_row)
+    blocks = np.asarray(blocks, dtype=np.int64)
+    nb = blocks.size
+    bits = np.zeros((nb, nwords(k, T)), dtype=np.uint32)
+    s0 = np.zeros(nb, dtype=np.uint32)
+    cost = np.zeros(nb, dtype=np.float32)
+    C = _f32(C)
+    dd = _f32(d)
+
+    def one(i):
+        b = int(blocks[i])
+        r, c = divmod(b, per_row)
+        wb = np.ascontiguousarray(W[r, c * T:(c + 1) * T])
+        db = None if dd is None else np.ascontiguousarray(dd[c * T:(c + 1) * T])
+        bb, ss, cc = encode_block(wb, db, C, L, k, V, T)
+        bits[i] = bb
+        s0[i] = ss
+        cost[i] = cc
+
+    if threads <= 1:
+        for i in range(nb):
+            one(i)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(nb)))
+    return bits, s0, cost
