@@ -1,0 +1,181 @@
+"""Throughput of the bitshift-trellis Viterbi encoder on one MI355X.
+
+One step = one tcq_encode call over the whole workload (every coding block: forward
+add-compare-select, backpointer store, traceback, packing), inputs resident in HBM.
+Default workload: the 2048 x 2048 N(0,1) projection, L=16, k=2, V=1, T=256, d = 1,
+65536-entry shuffled Gaussian-quantile codebook.
+
+Prints one JSON line (rank 0).  Alongside the throughput it reports the forward
+kernel's roofline (VALU-bound: algorithmic VALU operations per state update over the
+chip's VALU issue rate, timed live with HIP events around the forward launch) and the
+CPU oracle timed on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "weights encoded/s (L=16,k=2,T=256 Viterbi) + % VALU peak ACS ops/s"
+
+# MI355X: 256 compute units, 4 SIMDs x 16 lanes each (64 fp32 VALU lane-ops per clock
+# per CU, non-packed), 2.4 GHz peak engine clock.
+N_CU = 256
+LANES_PER_CU_CLK = 64
+CLOCK_HZ = 2.4e9
+VALU_PEAK_OPS = N_CU * LANES_PER_CU_CLK * CLOCK_HZ  # 3.93e13 lane-ops/s
+HBM_PEAK_GBPS = 8000.0
+
+
+def valu_ops_per_state_update(k: int, V: int, weighted: bool) -> float:
+    """Algorithmic VALU lane-ops per state update (one successor at one step):
+    per coordinate a subtract, a multiply by d (weighted only) and a fused multiply-add;
+    per group of G = 2^(kV) predecessors a tournament of G-1 minima and G-1 compares
+    (for the lowest-index argmin), shared by the group's G successors."""
+    G = 2 ** (k * V)
+    return V * (3.0 if weighted else 2.0) + 2.0 * (G - 1) / G
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=1, help="index into workloads.WORKLOADS")
+    ap.add_argument("--cpu-blocks", type=int, default=1024,
+                    help="blocks in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="0: min(16, cpu count)")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg, quiet=False):
+    if not quiet:
+        sys.stderr.write(msg + "\n")
+        sys.stderr.flush()
+
+
+def cpu_baseline(w, W, d, C, nblocks, threads):
+    import oracle
+    rng = np.random.default_rng(12345)
+    blocks = np.sort(rng.choice(w.blocks, size=min(nblocks, w.blocks), replace=False))
+    t0 = time.perf_counter()
+    oracle.encode_matrix(W, d, C, w.L, w.k, w.V, w.T, blocks=blocks, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": blocks.size * w.T / dt, "unit": "weights/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{blocks.size} seeded-random blocks of the same workload "
+                      f"({blocks.size * w.T} weights), one block per thread at a time, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every coding block is independent; see the sharding note in the docs)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from trellis_coded_bit_amd import _lib, api
+    from trellis_coded_bit_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    _lib.load()  # fail loudly if the HIP library is missing
+    w = wl.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: generating inputs", args.quiet)
+    W = wl.make_weights(w)
+    d = wl.make_d(w)
+    C = _lib.tcq_make_codebook(w.L, w.V, w.codebook_seed)
+    dev = torch.device("cuda:0")
+    Wt = torch.from_numpy(W).to(dev)
+    dt_ = None if d is None else torch.from_numpy(d).to(dev)
+    Ct = torch.from_numpy(C).to(dev)
+    nb = w.blocks
+    ws_bytes = _lib.tcq_encode_workspace_bytes(w.M, w.N, w.L, w.k, w.V, w.T)
+    ws = api.Workspace(ws_bytes, dev)
+    out = api.Encoded(
+        bitstream=torch.empty((nb, api.nwords(w.k, w.T)), dtype=torch.int32, device=dev),
+        start_state=torch.empty(nb, dtype=torch.int32, device=dev),
+        cost=torch.empty(nb, dtype=torch.float32, device=dev), recon=None)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:  # torch creates its events lazily, at the first record
+        a.record(stream)
+        b.record(stream)
+
+    def step(i=None):
+        e0, e1 = (None, None) if i is None else (ev[i][0].cuda_event, ev[i][1].cuda_event)
+        _lib.tcq_encode_timed(Wt.data_ptr(), w.M, w.N, w.N,
+                              None if dt_ is None else dt_.data_ptr(), Ct.data_ptr(), w.L,
+                              w.k, w.V, w.T, out.bitstream.data_ptr(),
+                              out.start_state.data_ptr(), out.cost.data_ptr(), None, w.N,
+                              ws.ptr, ws.nbytes, stream.cuda_stream, e0, e1)
+
+    log(f"[bench] warmup {args.warmup}", args.quiet)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps", args.quiet)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    acs_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    weights_per_s = w.weights / (ms_per_step / 1e3)
+
+    updates_per_launch = nb * (w.T // w.V) * (1 << w.L)
+    ops = valu_ops_per_state_update(w.k, w.V, d is not None)
+    acs_ops_per_s = updates_per_launch / (acs_ms / 1e3)
+    achieved_tops = acs_ops_per_s * ops / 1e12
+    peak_tops = VALU_PEAK_OPS / 1e12
+    bp_bytes = nb * (w.T // w.V) * (1 << (w.L - w.k * w.V)) * (w.k * w.V) / 8
+    bp_gbps = bp_bytes / (acs_ms / 1e3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": weights_per_s,
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "L": w.L, "k": w.k, "V": w.V,
+                   "T": w.T, "d": "weighted (LDL diagonal)" if d is not None else "1 (NULL)",
+                   "codebook": f"2^{w.L} shuffled Gaussian quantiles, seed {w.codebook_seed}"},
+        "roofline": {"bound": "alu", "achieved": achieved_tops, "peak": peak_tops,
+                     "unit": "TOP/s", "frac": achieved_tops / peak_tops, "traffic": None},
+        "acs": {"kernel_ms": acs_ms, "state_updates_per_s": acs_ops_per_s,
+                "valu_ops_per_update": ops, "valu_pct": 100.0 * achieved_tops / peak_tops,
+                "bp_write_GBps": bp_gbps, "bp_pct_hbm": 100.0 * bp_gbps / HBM_PEAK_GBPS,
+                "share_of_step": acs_ms / ms_per_step},
+    }
+    if args.cpu_blocks > 0:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        log(f"[bench] cpu oracle on {args.cpu_blocks} blocks, {threads} threads", args.quiet)
+        result["cpu_baseline"] = cpu_baseline(w, W, d, C, args.cpu_blocks, threads)
+    print(json.dumps(result))
+    sys.stdout.flush()
+
+
+if __name__ == "__main__":
+    main()

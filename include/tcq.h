@@ -1,0 +1,153 @@
+/*
+ * tcq.h -- C ABI of libtcq, a bitshift-trellis Viterbi encoder for AMD MI355X (gfx950).
+ *
+ * The operation (sources: QTIP abstract on the "QTIP: Quantization with Trellises and
+ * Incoherence Processing" summary page; the trellis-coded quantization paragraph, the
+ * 1-bit toy example and the Viterbi paragraph of the Pingala-8 post; the CurveTQ
+ * abstract on the aqora listing):
+ *
+ *   A weight matrix W (M x N, row-major) is cut into coding blocks of T consecutive
+ *   weights along each row: block b = r * (N/T) + c covers W[r, cT .. cT+T-1] and uses
+ *   the per-column weights d[cT .. cT+T-1].  Each block is coded as a path through a
+ *   "bitshift" trellis: an L-bit state s takes in kV fresh bits per step,
+ *       s_t = ((s_{t-1} << kV) | b_t) mod 2^L,          t = 1 .. n,  n = T / V,
+ *   and emits the V values C[s_t][0..V-1] of a 2^L-row lookup codebook.  The start
+ *   state s_0 < 2^(L-kV) is chosen freely per block.  The encoder returns, per block,
+ *   the path of minimum cost
+ *       J = sum_i d_i (w_i - what_i)^2
+ *   found by the Viterbi algorithm (the cheapest path into every state is kept).
+ *
+ * Arithmetic: fp32 throughout.  Each weight contributes, in order,
+ *       e = fl(w - c);  acc = fmaf(fl(d * e), e, acc)        (d == NULL: fmaf(e, e, acc))
+ * starting from acc = +0; at each step the predecessor kept for a state is the one
+ * with the smallest cost, the lowest predecessor index j on ties, where the
+ * predecessors of s' are (j << (L-kV)) | (s' >> kV), j = 0 .. 2^kV - 1.  The chosen end
+ * state is the lowest-index minimum.  Costs are never renormalised.
+ *
+ * Memory: every pointer argument of tcq_encode / tcq_decode is a DEVICE pointer owned
+ * by the caller (for instance torch tensors); the library never frees or retains them.
+ * Calls are asynchronous on `stream` (0 = the null stream); outputs are valid once the
+ * stream has completed.  Argument checks happen on the host, synchronously, before
+ * anything is enqueued; a call that returns an error has enqueued nothing.
+ * The library keeps no state between calls apart from the per-thread error string.
+ */
+#ifndef TCQ_H
+#define TCQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every entry point returns one of these. */
+typedef enum {
+    TCQ_OK = 0,
+    TCQ_EINVAL = -1,       /* bad argument (shape, divisibility, null pointer, stride) */
+    TCQ_EUNSUPPORTED = -2, /* valid trellis the GPU path does not handle (see limits) */
+    TCQ_EWORKSPACE = -3,   /* workspace missing or smaller than the minimum */
+    TCQ_EHIP = -4,         /* a HIP runtime call failed (message in tcq_last_error) */
+    TCQ_ENOMEM = -5        /* host allocation failed */
+} tcq_status;
+
+/* Limits of the GPU path: 2 <= L <= 16, 1 <= k*V <= min(L-1, 8), 1 <= V <= 4,
+ * 1 <= T/V <= 1024 steps per block. */
+#define TCQ_MAX_L 16
+#define TCQ_MAX_KV 8
+#define TCQ_MAX_V 4
+#define TCQ_MAX_STEPS 1024
+
+/* Library version as an integer (major * 10000 + minor * 100 + patch). */
+int tcq_version(void);
+
+/* Message describing the last failure on the calling thread ("" if none).  The
+ * pointer stays valid until the next call on the same thread. */
+const char *tcq_last_error(void);
+
+/*
+ * tcq_make_codebook -- the closed-form quantile table (CurveTQ abstract: "closed-form
+ * quantile table"), in a seeded shuffled order.
+ *   L, V      : 1 <= L <= 24, 1 <= V <= min(L, 8)
+ *   seed      : shuffle seed
+ *   out_host  : HOST buffer of 2^L * V floats, row-major [2^L][V]; written entirely.
+ * Row e of the unshuffled table is a product-grid point: the L bits of e are split into
+ * V fields (field 0 most significant; the first L mod V fields get one extra bit) and
+ * coordinate v is the Gaussian quantile Phi^-1((a + 1/2) / 2^bits_v) selected by field
+ * v (V = 1: the plain table Phi^-1((j + 1/2) / 2^L)).  Phi^-1 is Wichura's AS 241
+ * (1988) in double, rounded to float, and made exactly antisymmetric.  Rows are then
+ * shuffled by Fisher-Yates from the last row down, with j = SplitMix64(seed) mod (i+1).
+ * Host-only; touches no GPU.  Errors: TCQ_EINVAL.
+ */
+int tcq_make_codebook(int L, int V, uint64_t seed, float *out_host);
+
+/*
+ * tcq_encode_workspace_bytes -- device workspace size tcq_encode should be given to
+ * encode the whole M x N problem at full speed.  Any workspace of at least
+ * tcq_encode_workspace_min_bytes() also works (blocks are then processed in several
+ * batches on the stream).  Errors: TCQ_EINVAL, TCQ_EUNSUPPORTED.
+ */
+int tcq_encode_workspace_bytes(int64_t M, int64_t N, int L, int k, int V, int T,
+                               size_t *bytes);
+int tcq_encode_workspace_min_bytes(int L, int k, int V, int T, size_t *bytes);
+
+/*
+ * tcq_encode -- Viterbi-encode every coding block of W.
+ *   W          : device, M x N floats, row r at W + r * ldw (ldw >= N); finite values
+ *   d          : device, N floats >= 0 (finite), or NULL for d == 1 (plain Euclidean)
+ *   codebook   : device, 2^L * V floats, row-major [2^L][V]
+ *   L, k, V, T : trellis parameters; N % T == 0, T % V == 0, within the GPU limits
+ *   bitstream  : device out, [M * N / T][ceil(k*T/32)] uint32.  Block b's chunks
+ *                b_1 .. b_n (kV bits each, b_1 first, each most-significant bit
+ *                first) packed into words most-significant bit first; unused tail
+ *                bits are 0.
+ *   start_state: device out, [M * N / T] uint32, s_0 < 2^(L - kV)
+ *   cost       : device out, [M * N / T] float, the fp32 cost of the chosen path
+ *   recon      : device out or NULL; if given, M x N floats with row stride ldr >= N,
+ *                the reconstruction C[s_t][v] at every weight position
+ *   workspace  : device scratch of workspace_bytes (>= tcq_encode_workspace_min_bytes)
+ *   stream     : HIP stream the work is enqueued on
+ * M == 0 or N == 0 is a no-op.  Encoding a row range through pointer offsets gives
+ * bitwise the same results as those rows inside a whole-matrix call.
+ * Errors: TCQ_EINVAL, TCQ_EUNSUPPORTED, TCQ_EWORKSPACE, TCQ_EHIP.
+ */
+int tcq_encode(const float *W, int64_t M, int64_t N, int64_t ldw, const float *d,
+               const float *codebook, int L, int k, int V, int T, uint32_t *bitstream,
+               uint32_t *start_state, float *cost, float *recon, int64_t ldr,
+               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tcq_encode_timed -- tcq_encode, plus two events recorded on `stream` for profiling:
+ * `acs_begin` immediately before the first forward (add-compare-select) kernel launch
+ * and `acs_end` immediately after the last one.  Either event may be NULL.  With a
+ * workspace of tcq_encode_workspace_bytes() for problems whose blocks fit one batch
+ * there is exactly one forward launch, so hipEventElapsedTime(acs_begin, acs_end) is
+ * that kernel's duration; with several batches the span also covers the traceback
+ * launches interleaved between them.  Same outputs and errors as tcq_encode.
+ */
+int tcq_encode_timed(const float *W, int64_t M, int64_t N, int64_t ldw, const float *d,
+                     const float *codebook, int L, int k, int V, int T, uint32_t *bitstream,
+                     uint32_t *start_state, float *cost, float *recon, int64_t ldr,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream,
+                     hipEvent_t acs_begin, hipEvent_t acs_end);
+
+/*
+ * tcq_decode -- rebuild weights from bitstreams (Pingala-8 post: decoding reads bits,
+ * updates the state and looks up values).
+ *   bitstream, start_state : device, as written by tcq_encode for an M x N problem
+ *   codebook               : device, 2^L * V floats
+ *   out                    : device out, M x N floats with row stride ldo >= N;
+ *                            out[r, cT + (t-1)V + v] = C[s_t][v] of block r*(N/T)+c
+ * Errors: TCQ_EINVAL, TCQ_EUNSUPPORTED, TCQ_EHIP.
+ */
+int tcq_decode(const uint32_t *bitstream, const uint32_t *start_state, const float *codebook,
+               int64_t M, int64_t N, int L, int k, int V, int T, float *out, int64_t ldo,
+               hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TCQ_H */

@@ -1,0 +1,120 @@
+"""Host-side checks of libtcq: it loads, exports every symbol the header declares, its
+codebook builder agrees bit for bit with the oracle's, and argument checks reject bad
+calls before anything reaches a GPU (no device work is issued by these tests)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import trellis_coded_bit_amd as tcq
+from trellis_coded_bit_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000001000  # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "tcq.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(tcq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_declared_symbols():
+    lib = _lib.load()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert tcq.tcq_version() >= 100
+
+
+@pytest.mark.parametrize("L,V,seed", [(1, 1, 0), (2, 1, 42), (8, 1, 3000), (12, 1, 9),
+                                      (16, 1, 3001), (16, 2, 3004), (9, 2, 5), (10, 3, 77),
+                                      (16, 4, 1)])
+def test_codebook_matches_oracle(oracle_lib, L, V, seed):
+    lib_cb = tcq.tcq_make_codebook(L, V, seed)
+    ora_cb = oracle_lib.make_codebook(L, V, seed)
+    assert lib_cb.shape == ora_cb.shape
+    assert np.array_equal(lib_cb.view(np.uint32), ora_cb.view(np.uint32))
+
+
+def test_codebook_rejects_bad_args():
+    for L, V in [(0, 1), (25, 1), (4, 0), (3, 4), (16, 9)]:
+        with pytest.raises(tcq.TcqError) as ei:
+            tcq.tcq_make_codebook(L, V, 1)
+        assert ei.value.status == _lib.TCQ_EINVAL
+    assert _lib.load().tcq_make_codebook(4, 1, 0, None) == _lib.TCQ_EINVAL
+    assert "NULL" in tcq.tcq_last_error()
+
+
+def _enc(**kw):
+    args = dict(W=FAKE, M=4, N=256, ldw=256, d=None, codebook=FAKE, L=16, k=2, V=1, T=256,
+                bitstream=FAKE, start_state=FAKE, cost=FAKE, recon=None, ldr=256,
+                workspace=FAKE, workspace_bytes=1, stream=None)
+    args.update(kw)
+    lib = _lib.load()
+    return lib.tcq_encode(args["W"], args["M"], args["N"], args["ldw"], args["d"],
+                          args["codebook"], args["L"], args["k"], args["V"], args["T"],
+                          args["bitstream"], args["start_state"], args["cost"],
+                          args["recon"], args["ldr"], args["workspace"],
+                          args["workspace_bytes"], args["stream"])
+
+
+def test_encode_argument_checks():
+    E = _lib
+    assert _enc(N=250) == E.TCQ_EINVAL                  # N % T
+    assert _enc(T=255, V=2, N=255 * 4) == E.TCQ_EINVAL  # T % V
+    assert _enc(k=16, L=16) == E.TCQ_EINVAL             # kV == L
+    assert _enc(k=2, V=2, L=4, T=256) == E.TCQ_EINVAL   # kV == L with V > 1
+    assert _enc(k=9, L=8) == E.TCQ_EINVAL               # kV > L
+    assert _enc(M=-1) == E.TCQ_EINVAL
+    assert _enc(L=17) == E.TCQ_EUNSUPPORTED
+    assert _enc(k=3, V=3, T=255, N=255, L=16) == E.TCQ_EUNSUPPORTED  # kV = 9 > 8
+    assert _enc(V=5, T=260, N=260, L=16, k=1) == E.TCQ_EUNSUPPORTED
+    assert _enc(T=2048, N=2048) == E.TCQ_EUNSUPPORTED   # more than 1024 steps
+    assert _enc(ldw=100) == E.TCQ_EINVAL
+    assert _enc(W=None) == E.TCQ_EINVAL
+    assert _enc(codebook=None) == E.TCQ_EINVAL
+    assert _enc(bitstream=None) == E.TCQ_EINVAL
+    assert _enc(start_state=None) == E.TCQ_EINVAL
+    assert _enc(cost=None) == E.TCQ_EINVAL
+    assert _enc(recon=FAKE, ldr=3) == E.TCQ_EINVAL
+    assert _enc(workspace_bytes=16) == E.TCQ_EWORKSPACE
+    assert _enc(workspace=None, workspace_bytes=1 << 40) == E.TCQ_EWORKSPACE
+    assert "workspace" in tcq.tcq_last_error()
+    # empty problems are a no-op and touch nothing
+    assert _enc(M=0) == E.TCQ_OK
+    assert _enc(N=0, ldw=0) == E.TCQ_OK
+    assert tcq.tcq_last_error() == ""
+
+
+def test_decode_argument_checks():
+    lib = _lib.load()
+    E = _lib
+
+    def dec(**kw):
+        a = dict(bits=FAKE, s0=FAKE, cb=FAKE, M=2, N=512, L=16, k=2, V=1, T=256, out=FAKE,
+                 ldo=512)
+        a.update(kw)
+        return lib.tcq_decode(a["bits"], a["s0"], a["cb"], a["M"], a["N"], a["L"], a["k"],
+                              a["V"], a["T"], a["out"], a["ldo"], None)
+
+    assert dec(N=500) == E.TCQ_EINVAL
+    assert dec(bits=None) == E.TCQ_EINVAL
+    assert dec(out=None) == E.TCQ_EINVAL
+    assert dec(ldo=10) == E.TCQ_EINVAL
+    assert dec(L=20) == E.TCQ_EUNSUPPORTED
+    assert dec(M=0) == E.TCQ_OK
+
+
+def test_workspace_sizes():
+    mn = tcq.tcq_encode_workspace_min_bytes(16, 2, 1, 256)
+    full = tcq.tcq_encode_workspace_bytes(2048, 2048, 16, 2, 1, 256)
+    assert 0 < mn <= full
+    # backpointers alone are n * 2^(L-kV) * kV bits per block
+    assert mn >= 256 * (1 << 14) * 2 // 8
+    small = tcq.tcq_encode_workspace_bytes(64, 64, 8, 2, 1, 64)
+    assert small >= 64 * 64 * 64 * 2 // 8
+    with pytest.raises(tcq.TcqError):
+        tcq.tcq_encode_workspace_bytes(10, 100, 16, 2, 1, 256)

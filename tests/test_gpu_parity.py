@@ -1,0 +1,149 @@
+"""GPU encoder vs. the CPU oracle, through the C ABI (libtcq.so), on seeded inputs.
+
+Bar (see parity.py): per-block cost within 1e-5 relative, bitstream and start state
+identical unless the oracle's runner-up is within 1e-5 relative.  The canonical fp32
+order on both sides makes exact equality the expected outcome, and the tests also
+record that every block matched exactly.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import parity
+from trellis_coded_bit_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+from trellis_coded_bit_amd import api  # noqa: E402
+
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def _say(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+def _gpu_encode(W, d, C, L, k, V, T, recon=False, workspace=None):
+    Wt = torch.from_numpy(np.ascontiguousarray(W)).cuda()
+    dt = None if d is None else torch.from_numpy(np.ascontiguousarray(d)).cuda()
+    Ct = torch.from_numpy(np.ascontiguousarray(C)).cuda()
+    out = api.encode(Wt, dt, Ct, L, k, V, T, recon=recon, workspace=workspace)
+    torch.cuda.synchronize()
+    return (out.bitstream.cpu().numpy().view(np.uint32), out.start_state.cpu().numpy().view(np.uint32),
+            out.cost.cpu().numpy(), None if out.recon is None else out.recon.cpu().numpy())
+
+
+SMALL = [
+    # L, k, V, T, M, N, weighted
+    (4, 1, 1, 12, 5, 36, False),
+    (5, 2, 2, 10, 7, 40, True),
+    (6, 2, 1, 64, 9, 128, True),
+    (8, 2, 1, 64, 16, 256, False),
+    (8, 3, 1, 48, 10, 96, True),
+    (8, 2, 2, 32, 8, 96, True),
+    (9, 4, 1, 100, 6, 300, False),
+    (10, 1, 1, 200, 4, 400, True),
+    (10, 3, 2, 30, 6, 120, True),
+    (12, 2, 1, 256, 4, 512, True),
+    (12, 4, 2, 64, 3, 128, False),
+    (13, 2, 1, 96, 3, 192, True),
+    (14, 2, 1, 64, 2, 128, False),
+    (15, 3, 1, 40, 2, 80, True),
+    (16, 2, 1, 256, 2, 512, False),
+    (16, 2, 1, 256, 2, 512, True),
+    (16, 3, 1, 96, 2, 192, True),
+    (16, 2, 2, 128, 1, 256, True),
+    (16, 1, 1, 7, 1, 21, True),
+    (16, 2, 1, 1, 1, 3, True),
+]
+
+
+@pytest.mark.parametrize("L,k,V,T,M,N,weighted", SMALL)
+def test_parity_small(oracle_lib, L, k, V, T, M, N, weighted):
+    _say(f"case L={L} k={k} V={V} T={T} M={M} N={N} weighted={weighted}")
+    W, d = wl.random_small(1000 * L + 10 * k + V + T, M, N, weighted)
+    C = oracle_lib.make_codebook(L, V, 17 + L)
+    bits, s0, cost, recon = _gpu_encode(W, d, C, L, k, V, T, recon=True)
+    nb = M * (N // T)
+    rep = parity.compare(oracle_lib, W, d, C, L, k, V, T, np.arange(nb), bits, s0, cost,
+                         threads=THREADS)
+    assert rep.ok(), str(rep)
+    assert rep.exact == nb, str(rep)
+    # reconstruction == oracle decode of the GPU's own path
+    for b in range(nb):
+        r, c = divmod(b, N // T)
+        dec = oracle_lib.decode_block(bits[b], int(s0[b]), C, L, k, V, T)
+        assert np.array_equal(recon[r, c * T:(c + 1) * T], dec)
+
+
+def test_parity_tiny_workload_full(oracle_lib):
+    w = wl.WORKLOADS[0]
+    _say(f"workload {w.name}")
+    W = wl.make_weights(w)
+    C = oracle_lib.make_codebook(w.L, w.V, w.codebook_seed)
+    bits, s0, cost, _ = _gpu_encode(W, None, C, w.L, w.k, w.V, w.T)
+    rep = parity.compare(oracle_lib, W, None, C, w.L, w.k, w.V, w.T, np.arange(w.blocks), bits,
+                         s0, cost, threads=THREADS)
+    assert rep.ok() and rep.exact == w.blocks, str(rep)
+
+
+def test_decode_roundtrip_and_determinism(oracle_lib):
+    L, k, V, T, M, N = 16, 2, 1, 256, 3, 768
+    W, d = wl.random_small(5, M, N, True)
+    C = oracle_lib.make_codebook(L, V, 5)
+    b1, s1, c1, r1 = _gpu_encode(W, d, C, L, k, V, T, recon=True)
+    b2, s2, c2, r2 = _gpu_encode(W, d, C, L, k, V, T, recon=True)
+    assert np.array_equal(b1, b2) and np.array_equal(s1, s2)
+    assert np.array_equal(c1.view(np.uint32), c2.view(np.uint32))
+    Ct = torch.from_numpy(C).cuda()
+    dec = api.decode(torch.from_numpy(b1.view(np.int32)).cuda(),
+                     torch.from_numpy(s1.view(np.int32)).cuda(), Ct, M, N, L, k, V, T)
+    torch.cuda.synchronize()
+    assert np.array_equal(dec.cpu().numpy(), r1)
+
+
+def test_row_range_and_small_workspace(oracle_lib):
+    # a sub-range of rows through a pointer offset, and a workspace that forces one block
+    # per batch, both give the whole-matrix answer bit for bit
+    from trellis_coded_bit_amd import _lib
+    L, k, V, T, M, N = 12, 2, 1, 128, 6, 512
+    W, d = wl.random_small(8, M, N, True)
+    C = oracle_lib.make_codebook(L, V, 8)
+    full = _gpu_encode(W, d, C, L, k, V, T)
+    ws = api.Workspace(_lib.tcq_encode_workspace_min_bytes(L, k, V, T))
+    small = _gpu_encode(W, d, C, L, k, V, T, workspace=ws)
+    for a, b in zip(full[:3], small[:3]):
+        assert np.array_equal(np.asarray(a).view(np.uint32), np.asarray(b).view(np.uint32))
+    Wt = torch.from_numpy(W).cuda()
+    sub = Wt[2:5]
+    out = api.encode(sub, torch.from_numpy(d).cuda(), torch.from_numpy(C).cuda(), L, k, V, T)
+    torch.cuda.synchronize()
+    per_row = N // T
+    assert np.array_equal(out.bitstream.cpu().numpy().view(np.uint32),
+                          full[0][2 * per_row:5 * per_row])
+    assert np.array_equal(out.cost.cpu().numpy(), full[2][2 * per_row:5 * per_row])
+
+
+def test_strided_rows_and_empty(oracle_lib):
+    L, k, V, T, M, N = 10, 2, 1, 64, 4, 128
+    W, d = wl.random_small(9, M, 200, False)
+    C = oracle_lib.make_codebook(L, V, 9)
+    Wt = torch.from_numpy(W).cuda()[:, :N]       # ldw = 200 > N
+    assert Wt.stride(0) == 200
+    out = api.encode(Wt, None, torch.from_numpy(C).cuda(), L, k, V, T)
+    torch.cuda.synchronize()
+    Wc = np.ascontiguousarray(W[:, :N])
+    rep = parity.compare(oracle_lib, Wc, None, C, L, k, V, T, np.arange(M * N // T),
+                         out.bitstream.cpu().numpy(), out.start_state.cpu().numpy(),
+                         out.cost.cpu().numpy())
+    assert rep.ok() and rep.exact == M * N // T
+    empty = api.encode(torch.empty((0, N), device="cuda"), None, torch.from_numpy(C).cuda(),
+                       L, k, V, T)
+    assert empty.cost.numel() == 0

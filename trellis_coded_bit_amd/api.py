@@ -1,0 +1,77 @@
+"""Torch-facing helpers over the C ABI: allocate device buffers with torch, pass their
+addresses and the current stream to libtcq.  No arithmetic happens here."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+
+def nwords(k: int, T: int) -> int:
+    return (k * T + 31) // 32
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class Encoded:
+    bitstream: torch.Tensor    # uint32 [blocks, nwords] (stored as int32)
+    start_state: torch.Tensor  # uint32 [blocks] (stored as int32)
+    cost: torch.Tensor         # float32 [blocks]
+    recon: torch.Tensor | None  # float32 [M, N]
+
+
+class Workspace:
+    """Device workspace owned by torch's allocator."""
+
+    def __init__(self, nbytes: int, device="cuda"):
+        self.nbytes = int(nbytes)
+        self.buf = torch.empty(max(self.nbytes, 1), dtype=torch.uint8, device=device)
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+
+def make_codebook(L: int, V: int, seed: int, device="cuda") -> torch.Tensor:
+    host = _lib.tcq_make_codebook(L, V, seed)
+    return torch.from_numpy(host).to(device)
+
+
+def encode(W: torch.Tensor, d: torch.Tensor | None, codebook: torch.Tensor, L: int, k: int,
+           V: int, T: int, recon: bool = False, workspace: Workspace | None = None,
+           out: Encoded | None = None) -> Encoded:
+    assert W.is_cuda and W.dtype == torch.float32 and W.dim() == 2 and W.stride(1) == 1
+    M, N = W.shape
+    assert codebook.is_cuda and codebook.dtype == torch.float32 and codebook.is_contiguous()
+    if d is not None:
+        assert d.is_cuda and d.dtype == torch.float32 and d.is_contiguous() and d.numel() == N
+    nb = M * (N // T) if T > 0 else 0
+    if out is None:
+        dev = W.device
+        out = Encoded(
+            bitstream=torch.empty((nb, nwords(k, T)), dtype=torch.int32, device=dev),
+            start_state=torch.empty(nb, dtype=torch.int32, device=dev),
+            cost=torch.empty(nb, dtype=torch.float32, device=dev),
+            recon=torch.empty((M, N), dtype=torch.float32, device=dev) if recon else None)
+    if workspace is None:
+        workspace = Workspace(_lib.tcq_encode_workspace_bytes(M, N, L, k, V, T), W.device)
+    _lib.tcq_encode(W.data_ptr(), M, N, W.stride(0), None if d is None else d.data_ptr(),
+                    codebook.data_ptr(), L, k, V, T, out.bitstream.data_ptr(),
+                    out.start_state.data_ptr(), out.cost.data_ptr(),
+                    None if out.recon is None else out.recon.data_ptr(),
+                    N if out.recon is None else out.recon.stride(0), workspace.ptr,
+                    workspace.nbytes, _stream())
+    return out
+
+
+def decode(bitstream: torch.Tensor, start_state: torch.Tensor, codebook: torch.Tensor, M: int,
+           N: int, L: int, k: int, V: int, T: int) -> torch.Tensor:
+    out = torch.empty((M, N), dtype=torch.float32, device=bitstream.device)
+    _lib.tcq_decode(bitstream.data_ptr(), start_state.data_ptr(), codebook.data_ptr(), M, N,
+                    L, k, V, T, out.data_ptr(), N, _stream())
+    return out

@@ -1,0 +1,264 @@
+// libtcq C ABI: argument checks, workspace planning, and launch ordering on the
+// caller's stream.  Every numeric step runs in the HIP kernels.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "tcq.h"
+#include "tcq_internal.h"
+
+namespace tcq {
+
+namespace {
+thread_local std::string g_error;
+
+// Blocks whose backpointers are kept in the workspace at once by the recommended size.
+constexpr int64_t kRecommendedBatchBytes = int64_t{24} << 30;  // per-block data cap
+constexpr int64_t kMinRecommendedBatch = 1024;
+}  // namespace
+
+void set_error(const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_error = buf;
+}
+
+static void clear_error() { g_error.clear(); }
+
+Plan plan_for(const Problem &p) {
+    Plan pl{};
+    if (l16_supported(p)) {
+        pl.variant = kL16Regs;
+        pl.fixed = align_up(l16_fixed_bytes(p), 256);
+        pl.bp_bytes = align_up(l16_bp_bytes(p), 256);
+        pl.cost_bytes = 0;
+    } else {
+        const int64_t nw64 = (p.ngroups + 63) / 64;
+        pl.bp_bytes = align_up(static_cast<size_t>(p.n) * p.kv * nw64 * 8, 256);
+        if (p.L <= 13) {
+            pl.variant = kGenericLds;
+            pl.cost_bytes = 0;
+        } else {
+            pl.variant = kGenericGlobal;
+            pl.cost_bytes = align_up(2 * static_cast<size_t>(p.nstates) * sizeof(float), 256);
+        }
+        pl.fixed = 0;
+    }
+    // per block: backpointers, cost buffers, and the chosen end state (4 bytes)
+    pl.per_block = pl.bp_bytes + pl.cost_bytes + sizeof(uint32_t);
+    return pl;
+}
+
+// Shared shape checks for encode and decode.
+static int check_trellis(const char *fn, int64_t M, int64_t N, int L, int k, int V, int T) {
+    if (M < 0 || N < 0) {
+        set_error("%s: negative matrix size (M=%lld N=%lld)", fn, (long long)M, (long long)N);
+        return TCQ_EINVAL;
+    }
+    if (L < 1 || k < 1 || V < 1 || T < 1) {
+        set_error("%s: L, k, V, T must be positive (L=%d k=%d V=%d T=%d)", fn, L, k, V, T);
+        return TCQ_EINVAL;
+    }
+    if (T % V != 0) {
+        set_error("%s: T=%d is not a multiple of V=%d", fn, T, V);
+        return TCQ_EINVAL;
+    }
+    if (N % T != 0) {
+        set_error("%s: N=%lld is not a multiple of T=%d", fn, (long long)N, T);
+        return TCQ_EINVAL;
+    }
+    if (static_cast<int64_t>(k) * V >= L) {
+        set_error("%s: need k*V < L (k=%d V=%d L=%d)", fn, k, V, L);
+        return TCQ_EINVAL;
+    }
+    if (L > TCQ_MAX_L || k * V > TCQ_MAX_KV || V > TCQ_MAX_V || T / V > TCQ_MAX_STEPS ||
+        L < 2) {
+        set_error("%s: outside the GPU limits (2<=L<=%d, k*V<=%d, V<=%d, T/V<=%d): "
+                  "L=%d k=%d V=%d T=%d",
+                  fn, TCQ_MAX_L, TCQ_MAX_KV, TCQ_MAX_V, TCQ_MAX_STEPS, L, k, V, T);
+        return TCQ_EUNSUPPORTED;
+    }
+    return TCQ_OK;
+}
+
+static Problem make_problem(int64_t M, int64_t N, int64_t ldw, int L, int k, int V, int T) {
+    Problem p{};
+    p.L = L;
+    p.k = k;
+    p.V = V;
+    p.T = T;
+    p.kv = k * V;
+    p.n = T / V;
+    p.M = M;
+    p.N = N;
+    p.ldw = ldw;
+    p.blocks_per_row = N / T;
+    p.nblocks = M * (N / T);
+    p.ngroups = int64_t{1} << (L - p.kv);
+    p.nstates = int64_t{1} << L;
+    return p;
+}
+
+static int hip_fail(const char *fn, const char *what, hipError_t e) {
+    set_error("%s: %s failed: %s", fn, what, hipGetErrorString(e));
+    return TCQ_EHIP;
+}
+
+}  // namespace tcq
+
+using namespace tcq;
+
+extern "C" int tcq_version(void) { return 100; }
+
+extern "C" const char *tcq_last_error(void) { return g_error.c_str(); }
+
+extern "C" int tcq_encode_workspace_min_bytes(int L, int k, int V, int T, size_t *bytes) {
+    clear_error();
+    int rc = check_trellis("tcq_encode_workspace_min_bytes", 1, T, L, k, V, T);
+    if (rc != TCQ_OK) return rc;
+    if (!bytes) {
+        set_error("tcq_encode_workspace_min_bytes: bytes is NULL");
+        return TCQ_EINVAL;
+    }
+    Problem p = make_problem(1, T, T, L, k, V, T);
+    Plan pl = plan_for(p);
+    *bytes = pl.fixed + 256 + pl.per_block;
+    return TCQ_OK;
+}
+
+extern "C" int tcq_encode_workspace_bytes(int64_t M, int64_t N, int L, int k, int V, int T,
+                                          size_t *bytes) {
+    clear_error();
+    int rc = check_trellis("tcq_encode_workspace_bytes", M, N, L, k, V, T);
+    if (rc != TCQ_OK) return rc;
+    if (!bytes) {
+        set_error("tcq_encode_workspace_bytes: bytes is NULL");
+        return TCQ_EINVAL;
+    }
+    Problem p = make_problem(M, N, N, L, k, V, T);
+    Plan pl = plan_for(p);
+    int64_t batch = kRecommendedBatchBytes / static_cast<int64_t>(pl.per_block);
+    if (batch < kMinRecommendedBatch) batch = kMinRecommendedBatch;
+    if (batch > p.nblocks) batch = p.nblocks;
+    if (batch < 1) batch = 1;
+    *bytes = pl.fixed + 256 + pl.per_block * static_cast<size_t>(batch);
+    return TCQ_OK;
+}
+
+static int encode_impl(const char *fn, const float *W, int64_t M, int64_t N, int64_t ldw,
+                       const float *d, const float *codebook, int L, int k, int V, int T,
+                       uint32_t *bitstream, uint32_t *start_state, float *cost, float *recon,
+                       int64_t ldr, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream, hipEvent_t acs_begin, hipEvent_t acs_end) {
+    clear_error();
+    int rc = check_trellis(fn, M, N, L, k, V, T);
+    if (rc != TCQ_OK) return rc;
+    if (M == 0 || N == 0) return TCQ_OK;
+    if (ldw < N) {
+        set_error("%s: ldw=%lld < N=%lld", fn, (long long)ldw, (long long)N);
+        return TCQ_EINVAL;
+    }
+    if (!W || !codebook || !bitstream || !start_state || !cost) {
+        set_error("%s: W, codebook, bitstream, start_state and cost must be non-NULL", fn);
+        return TCQ_EINVAL;
+    }
+    if (recon && ldr < N) {
+        set_error("%s: ldr=%lld < N=%lld", fn, (long long)ldr, (long long)N);
+        return TCQ_EINVAL;
+    }
+    Problem p = make_problem(M, N, ldw, L, k, V, T);
+    Plan pl = plan_for(p);
+    const size_t need = pl.fixed + 256 + pl.per_block;
+    if (!workspace || workspace_bytes < need) {
+        set_error("%s: workspace of %zu bytes is below the minimum %zu", fn,
+                  workspace ? workspace_bytes : size_t{0}, need);
+        return TCQ_EWORKSPACE;
+    }
+    int64_t batch = static_cast<int64_t>((workspace_bytes - pl.fixed - 256) / pl.per_block);
+    if (batch > p.nblocks) batch = p.nblocks;
+    if (batch > (int64_t{1} << 30)) batch = int64_t{1} << 30;
+    char *ws = static_cast<char *>(workspace);
+
+    hipError_t e;
+    if (pl.variant == kL16Regs) {
+        e = launch_l16_prepare(p, codebook, ws, stream);
+        if (e != hipSuccess) return hip_fail(fn, "codebook preparation launch", e);
+    }
+    for (int64_t b0 = 0; b0 < p.nblocks; b0 += batch) {
+        const int64_t nb = (p.nblocks - b0 < batch) ? p.nblocks - b0 : batch;
+        if (b0 == 0 && acs_begin) {
+            e = hipEventRecord(acs_begin, stream);
+            if (e != hipSuccess) return hip_fail(fn, "hipEventRecord", e);
+        }
+        if (pl.variant == kL16Regs) {
+            e = launch_acs_l16(p, pl, W, d, b0, nb, ws, cost, stream);
+            if (e != hipSuccess) return hip_fail(fn, "ACS launch", e);
+            if (b0 + nb >= p.nblocks && acs_end) {
+                e = hipEventRecord(acs_end, stream);
+                if (e != hipSuccess) return hip_fail(fn, "hipEventRecord", e);
+            }
+            e = launch_traceback_l16(p, pl, b0, nb, ws, bitstream, start_state, stream);
+            if (e != hipSuccess) return hip_fail(fn, "traceback launch", e);
+        } else {
+            e = launch_acs_generic(p, pl, W, d, codebook, b0, nb, ws, cost, stream);
+            if (e != hipSuccess) return hip_fail(fn, "ACS launch", e);
+            if (b0 + nb >= p.nblocks && acs_end) {
+                e = hipEventRecord(acs_end, stream);
+                if (e != hipSuccess) return hip_fail(fn, "hipEventRecord", e);
+            }
+            e = launch_traceback_planes(p, pl, b0, nb, ws, bitstream, start_state, stream);
+            if (e != hipSuccess) return hip_fail(fn, "traceback launch", e);
+        }
+    }
+    if (recon) {
+        e = launch_decode(bitstream, start_state, codebook, M, N, L, k, V, T, recon, ldr, stream);
+        if (e != hipSuccess) return hip_fail(fn, "reconstruction launch", e);
+    }
+    return TCQ_OK;
+}
+
+extern "C" int tcq_encode(const float *W, int64_t M, int64_t N, int64_t ldw, const float *d,
+                          const float *codebook, int L, int k, int V, int T,
+                          uint32_t *bitstream, uint32_t *start_state, float *cost,
+                          float *recon, int64_t ldr, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    return encode_impl("tcq_encode", W, M, N, ldw, d, codebook, L, k, V, T, bitstream,
+                       start_state, cost, recon, ldr, workspace, workspace_bytes, stream,
+                       nullptr, nullptr);
+}
+
+extern "C" int tcq_encode_timed(const float *W, int64_t M, int64_t N, int64_t ldw,
+                                const float *d, const float *codebook, int L, int k, int V,
+                                int T, uint32_t *bitstream, uint32_t *start_state,
+                                float *cost, float *recon, int64_t ldr, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t acs_begin, hipEvent_t acs_end) {
+    return encode_impl("tcq_encode_timed", W, M, N, ldw, d, codebook, L, k, V, T, bitstream,
+                       start_state, cost, recon, ldr, workspace, workspace_bytes, stream,
+                       acs_begin, acs_end);
+}
+
+extern "C" int tcq_decode(const uint32_t *bitstream, const uint32_t *start_state,
+                          const float *codebook, int64_t M, int64_t N, int L, int k, int V,
+                          int T, float *out, int64_t ldo, hipStream_t stream) {
+    clear_error();
+    const char *fn = "tcq_decode";
+    int rc = check_trellis(fn, M, N, L, k, V, T);
+    if (rc != TCQ_OK) return rc;
+    if (M == 0 || N == 0) return TCQ_OK;
+    if (!bitstream || !start_state || !codebook || !out) {
+        set_error("%s: bitstream, start_state, codebook and out must be non-NULL", fn);
+        return TCQ_EINVAL;
+    }
+    if (ldo < N) {
+        set_error("%s: ldo=%lld < N=%lld", fn, (long long)ldo, (long long)N);
+        return TCQ_EINVAL;
+    }
+    hipError_t e = launch_decode(bitstream, start_state, codebook, M, N, L, k, V, T, out, ldo,
+                                 stream);
+    if (e != hipSuccess) return hip_fail(fn, "decode launch", e);
+    return TCQ_OK;
+}

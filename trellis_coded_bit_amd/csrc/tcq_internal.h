@@ -1,0 +1,66 @@
+// Internal declarations shared by the sources of libtcq (not part of the ABI).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace tcq {
+
+// Shape of one encode problem after validation.
+struct Problem {
+    int L, k, V, T;
+    int kv;            // k * V: fresh bits per step
+    int n;             // steps per block, T / V
+    int64_t M, N;
+    int64_t ldw;
+    int64_t blocks_per_row;
+    int64_t nblocks;
+    int64_t ngroups;   // 2^(L - kv)
+    int64_t nstates;   // 2^L
+};
+
+// Workspace plan for one kernel family: per-block bytes, fixed bytes.
+struct Plan {
+    int variant;              // see kernels
+    size_t per_block;         // bytes per block in flight
+    size_t fixed;             // bytes independent of the batch size
+    size_t bp_bytes;          // backpointer bytes per block
+    size_t cost_bytes;        // global cost-vector bytes per block (0: on chip)
+};
+
+enum Variant : int {
+    kGenericLds = 0,     // any supported shape, cost vectors double-buffered in LDS
+    kGenericGlobal = 1,  // any supported shape, cost vectors in the workspace (L2)
+    kL16Regs = 2,        // L = 16, six active bits per super-step, costs in VGPRs
+};
+
+Plan plan_for(const Problem &p);
+
+// Kernel launchers (return hipError_t of the launch).
+hipError_t launch_acs_generic(const Problem &p, const Plan &pl, const float *W,
+                              const float *d, const float *C, int64_t block0, int64_t nb,
+                              char *ws, float *cost, hipStream_t s);
+hipError_t launch_traceback_planes(const Problem &p, const Plan &pl, int64_t block0,
+                                   int64_t nb, const char *ws, uint32_t *bitstream,
+                                   uint32_t *start_state, hipStream_t s);
+hipError_t launch_decode(const uint32_t *bitstream, const uint32_t *start_state,
+                         const float *C, int64_t M, int64_t N, int L, int k, int V, int T,
+                         float *out, int64_t ldo, hipStream_t s);
+
+// L = 16 register-resident path.
+bool l16_supported(const Problem &p);
+size_t l16_fixed_bytes(const Problem &p);
+size_t l16_bp_bytes(const Problem &p);
+hipError_t launch_l16_prepare(const Problem &p, const float *C, char *fixed_ws, hipStream_t s);
+hipError_t launch_acs_l16(const Problem &p, const Plan &pl, const float *W, const float *d,
+                          int64_t block0, int64_t nb, char *ws, float *cost, hipStream_t s);
+hipError_t launch_traceback_l16(const Problem &p, const Plan &pl, int64_t block0, int64_t nb,
+                                const char *ws, uint32_t *bitstream, uint32_t *start_state,
+                                hipStream_t s);
+
+// Workspace layout helpers: [fixed area][per-block area x batch]
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace tcq
