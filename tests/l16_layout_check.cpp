@@ -1,0 +1,118 @@
+// Host-side check of the L = 16 kernel's index math (l16_layout.h), compiled with g++
+// by test_l16_layout.py.  Verifies, exhaustively over all 2^16 slots:
+//  - state_of(p, .) is a bijection slots -> states and slot_of(p, .) is its inverse;
+//  - the four registers of a group at step p hold the four predecessors of one group
+//    (states that differ only in the oldest digit) at p-1, and the successors with
+//    new digit b = 0..3 at p;
+//  - the transposition moves the value of each state at p = 3 to the slot that holds
+//    the same state at p = 0;
+//  - LDS staging addresses are in range, distinct within a round, agree between the
+//    writing and the reading side, and every wave instruction touches distinct banks
+//    (64 banks per wave, 32 per half wave).
+#define __host__
+#define __device__
+#include <cstdio>
+#include <cstdlib>
+#include <set>
+#include <vector>
+
+#include "l16_layout.h"
+
+using namespace tcq::l16;
+
+static int fails = 0;
+#define CHECK(c)                                                         \
+    do {                                                                 \
+        if (!(c)) {                                                      \
+            if (fails < 20) std::printf("FAIL %s:%d %s\n", __FILE__, __LINE__, #c); \
+            ++fails;                                                     \
+        }                                                                \
+    } while (0)
+
+int main() {
+    // bijection and inverse
+    for (int p = 0; p <= 3; ++p) {
+        std::vector<int> seen(1 << 16, 0);
+        for (uint32_t w = 0; w < 8; ++w)
+            for (uint32_t l = 0; l < 64; ++l)
+                for (uint32_t r = 0; r < 128; ++r) {
+                    uint32_t s = state_of(p, w, l, r);
+                    CHECK(s < (1u << 16));
+                    seen[s]++;
+                    Slot q = slot_of(p, s);
+                    CHECK(q.w == w && q.l == l && q.r == r);
+                }
+        for (int s = 0; s < (1 << 16); ++s) CHECK(seen[s] == 1);
+    }
+    // group structure
+    for (int p = 1; p <= 3; ++p)
+        for (uint32_t w = 0; w < 8; ++w)
+            for (uint32_t l = 0; l < 64; ++l)
+                for (uint32_t g = 0; g < 32; ++g) {
+                    uint32_t x = state_of(p - 1, w, l, group_reg(p, g, 0)) & 0x3FFFu;
+                    for (uint32_t j = 0; j < 4; ++j) {
+                        uint32_t r = group_reg(p, g, j);
+                        CHECK(r < 128);
+                        CHECK(reg_group(p, r) == g);
+                        // predecessor j of the group: (j << 14) | x
+                        CHECK(state_of(p - 1, w, l, r) == ((j << 14) | x));
+                        // successor with new digit b = j: (x << 2) | j
+                        CHECK(state_of(p, w, l, r) == ((x << 2) | j));
+                    }
+                }
+    // transposition
+    {
+        std::set<uint32_t> dests;
+        for (uint32_t w = 0; w < 8; ++w)
+            for (uint32_t l = 0; l < 64; ++l)
+                for (uint32_t r = 0; r < 128; ++r) {
+                    Slot d = transpose_dest(w, l, r);
+                    CHECK(d.w < 8 && d.l < 64 && d.r < 128);
+                    CHECK(state_of(3, w, l, r) == state_of(0, d.w, d.l, d.r));
+                    CHECK(((d.r & 1u) == ((r >> 6) & 1u)));  // round split
+                    dests.insert((d.w << 13) | (d.l << 7) | d.r);
+                    CHECK(lds_write_lane(w, l) + lds_write_reg(r) ==
+                          lds_read_lane(d.w, d.l) + lds_read_reg(d.r));
+                }
+        CHECK(dests.size() == (1u << 16));
+    }
+    // LDS addresses: range, injectivity per round, banks
+    for (uint32_t rho = 0; rho < 2; ++rho) {
+        std::vector<int> used(kLdsDwords, 0);
+        for (uint32_t w = 0; w < 8; ++w)
+            for (uint32_t r = 0; r < 128; ++r) {
+                if (((r >> 6) & 1u) != rho) continue;
+                std::set<uint32_t> b64, b32lo, b32hi;
+                for (uint32_t l = 0; l < 64; ++l) {
+                    uint32_t a = lds_write_lane(w, l) + lds_write_reg(r);
+                    CHECK(a < kLdsDwords);
+                    if (a < kLdsDwords) used[a]++;
+                    b64.insert(a % 64);
+                    (l < 32 ? b32lo : b32hi).insert(a % 32);
+                }
+                CHECK(b64.size() == 64 && b32lo.size() == 32 && b32hi.size() == 32);
+            }
+        int dup = 0;
+        for (auto u : used) dup += (u > 1);
+        CHECK(dup == 0);
+        for (uint32_t w = 0; w < 8; ++w)
+            for (uint32_t r = 0; r < 128; ++r) {
+                if ((r & 1u) != rho) continue;
+                std::set<uint32_t> b64, b32lo, b32hi;
+                for (uint32_t l = 0; l < 64; ++l) {
+                    uint32_t a = lds_read_lane(w, l) + lds_read_reg(r);
+                    CHECK(a < kLdsDwords);
+                    if (a < kLdsDwords) CHECK(used[a] == 1);
+                    b64.insert(a % 64);
+                    (l < 32 ? b32lo : b32hi).insert(a % 32);
+                }
+                CHECK(b64.size() == 64 && b32lo.size() == 32 && b32hi.size() == 32);
+            }
+    }
+    if (fails) {
+        std::printf("%d failures\n", fails);
+        return 1;
+    }
+    std::printf("l16 layout ok\n");
+    return 0;
+}

@@ -1,0 +1,57 @@
+"""Full-size workloads on the GPU, in the launch configuration bench.py times (whole
+matrix, recommended workspace), checked against the oracle on sampled blocks: a seeded
+uniform sample plus every block of the first and last rows.  Bar as in parity.py."""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import parity
+from trellis_coded_bit_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+from trellis_coded_bit_amd import _lib, api  # noqa: E402
+
+THREADS = min(16, os.cpu_count() or 1)
+SAMPLE = int(os.environ.get("TCQ_TEST_SAMPLE_BLOCKS", "48"))
+
+
+def _say(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4])
+def test_workload_sampled_parity(oracle_lib, index):
+    w = wl.WORKLOADS[index]
+    t0 = time.time()
+    _say(f"workload {w.name}: generating inputs")
+    W = wl.make_weights(w)
+    d = wl.make_d(w)
+    C = _lib.tcq_make_codebook(w.L, w.V, w.codebook_seed)
+    assert np.array_equal(C, oracle_lib.make_codebook(w.L, w.V, w.codebook_seed))
+    _say(f"  inputs ready in {time.time() - t0:.1f}s; encoding {w.blocks} blocks on the GPU")
+    dev = torch.device("cuda:0")
+    out = api.encode(torch.from_numpy(W).to(dev), None if d is None else torch.from_numpy(d).to(dev),
+                     torch.from_numpy(C).to(dev), w.L, w.k, w.V, w.T)
+    torch.cuda.synchronize()
+    _say(f"  GPU done at {time.time() - t0:.1f}s")
+    blocks = wl.sample_blocks(w, SAMPLE, seed=100 + index)
+    bits = out.bitstream.cpu().numpy().view(np.uint32)[blocks]
+    s0 = out.start_state.cpu().numpy().view(np.uint32)[blocks]
+    cost = out.cost.cpu().numpy()[blocks]
+    rep = parity.compare(oracle_lib, W, d, C, w.L, w.k, w.V, w.T, blocks, bits, s0, cost,
+                         threads=THREADS)
+    _say(f"  {len(blocks)} blocks checked at {time.time() - t0:.1f}s: {rep}")
+    assert rep.ok(), str(rep)
+    # every cost is finite and start states are in range
+    allc = out.cost.cpu().numpy()
+    assert np.all(np.isfinite(allc))
+    assert np.all(out.start_state.cpu().numpy().view(np.uint32) < (1 << (w.L - w.k * w.V)))
