@@ -53,6 +53,9 @@ def parse():
                     help="blocks in the CPU-oracle sample (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="0: min(16, cpu count)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a device-to-device copy of BYTES bytes (reference for "
+                         "the HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -92,6 +95,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}))
+        return
     _lib.load()  # fail loudly if the HIP library is missing
     w = wl.WORKLOADS[args.workload]
     log(f"[bench] workload {w.name}: generating inputs", args.quiet)

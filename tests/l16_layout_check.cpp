@@ -109,6 +109,40 @@ int main() {
                 CHECK(b64.size() == 64 && b32lo.size() == 32 && b32hi.size() == 32);
             }
     }
+    // segment order: every (step, group) exactly once per super-step; step 1/2 halves
+    // follow register bit 0, step 3 halves follow register bit 6; backpointer slots
+    // are distinct per (step, group)
+    for (int p = 1; p <= 3; ++p) {
+        std::set<uint32_t> gs, slots;
+        for (int seg = 0; seg < 6; ++seg) {
+            if (seg_step(seg) != p) continue;
+            for (int i = 0; i < 16; ++i) {
+                uint32_t g = seg_group(seg, i);
+                CHECK(g < 32);
+                gs.insert(g);
+                CHECK(bp_half(p, g) == (uint32_t)seg_half(seg));
+                CHECK(bp_shift(p, g) == 2u * (15u - (uint32_t)i));
+                slots.insert(bp_half(p, g) * 32 + bp_shift(p, g));
+                for (uint32_t b = 0; b < 4; ++b) {
+                    uint32_t r = group_reg(p, g, b);
+                    if (p < 3) CHECK((r & 1u) == (uint32_t)seg_half(seg));
+                    else CHECK(((r >> 6) & 1u) == (uint32_t)seg_half(seg));
+                }
+            }
+        }
+        CHECK(gs.size() == 32 && slots.size() == 32);
+    }
+    // naming: each LDS round reads into the physical registers it wrote out
+    for (int m = 0; m < 2; ++m)
+        for (int rho = 0; rho < 2; ++rho) {
+            std::set<uint32_t> out, in;
+            for (uint32_t r = 0; r < 128; ++r) {
+                if (((r >> 6) & 1u) == (uint32_t)rho) out.insert(phys(m, r));
+                if ((r & 1u) == (uint32_t)rho) in.insert(phys(1 - m, r));
+            }
+            CHECK(out == in && out.size() == 64);
+        }
+    for (uint32_t r = 0; r < 128; ++r) CHECK(phys(1, phys(1, r)) == r && phys(0, r) == r);
     if (fails) {
         std::printf("%d failures\n", fails);
         return 1;

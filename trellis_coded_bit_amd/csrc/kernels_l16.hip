@@ -19,6 +19,8 @@
 #include "tcq.h"
 #include "tcq_internal.h"
 
+#include <utility>
+
 namespace tcq {
 namespace {
 
@@ -26,7 +28,7 @@ using namespace l16;
 
 constexpr int kThreads = kWaves * kLanes;  // 512
 constexpr int kCopy = kWaves * kGroupsPerLane * kLanes;  // float4 entries per copy
-constexpr int kPrefetch = 8;                            // groups of codebook in flight
+constexpr int kPrefetch = 12;                           // groups of codebook in flight
 
 __global__ __launch_bounds__(256) void l16_prepare_kernel(const float *__restrict__ C,
                                                           float4 *__restrict__ out) {
@@ -42,11 +44,48 @@ __global__ __launch_bounds__(256) void l16_prepare_kernel(const float *__restric
     out[idx] = make_float4(src[0], src[1], src[2], src[3]);
 }
 
+// Codebook copy entry for group g of step P: a raw buffer load whose per-lane offset
+// (voff = 16 * lane) is shared by every load and whose group/step offset is a scalar.
+// The low part of the offset ((g mod 4) KiB) goes to the instruction's immediate field,
+// so a super-step needs only 24 distinct scalar offsets.
+template <int P>
+__device__ __forceinline__ float4 cb_load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int g) {
+    constexpr int kEntry = static_cast<int>(sizeof(float4));
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+        rs, voff + (g & 3) * kLanes * kEntry, ((P - 1) * kCopy + (g & ~3) * kLanes) * kEntry, 0);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                       __uint_as_float(v[3]));
+}
+
+// The codebook entries are consumed in the fixed segment order of a super-step
+// (position k = 16 * segment + i, 96 per super-step); a ring of kPrefetch loads runs
+// ahead of the consumer, across segment and super-step boundaries.
+constexpr int kPositions = 96;
+
+template <int K>
+__device__ __forceinline__ float4 cb_load_pos(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+    constexpr int k = K % kPositions;
+    return cb_load<seg_step(k / 16)>(rs, voff, seg_group(k / 16, k % 16));
+}
+
+template <int K0, int... I>
+__device__ __forceinline__ void ring_prime(float4 (&ring)[kPrefetch], __amdgpu_buffer_rsrc_t rs,
+                                           uint32_t voff, std::integer_sequence<int, I...>) {
+    ((ring[(K0 + I) % kPrefetch] = cb_load_pos<K0 + I>(rs, voff)), ...);
+}
+
+// Fill the ring with positions K0 .. K0 + kPrefetch - 1.
+template <int K0>
+__device__ __forceinline__ void ring_fill(float4 (&ring)[kPrefetch], __amdgpu_buffer_rsrc_t rs,
+                                          uint32_t voff) {
+    ring_prime<K0>(ring, rs, voff, std::make_integer_sequence<int, kPrefetch>{});
+}
+
 // Shift one bit per lane, taken from a wave-wide compare mask, into acc:
 // acc = 2 * acc + mask[lane] in a single VALU op (carry-in from an SGPR pair).
 __device__ __forceinline__ uint32_t shift_in(uint32_t acc, uint64_t mask) {
     uint32_t r;
-    asm("v_addc_co_u32 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(acc), "s"(mask) : "vcc");
+    asm volatile("v_addc_co_u32 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(acc), "s"(mask) : "vcc");
     return r;
 }
 
@@ -54,76 +93,141 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t acc, uint64_t mask) {
 // -0), so their bit patterns order exactly like their values: minima and compares run
 // on the unsigned bit patterns, which needs no NaN canonicalization.
 //
-// Codebook copy entry for group g of step P: a raw buffer load whose per-lane offset
-// (voff = 16 * lane) is shared by every load and whose group/step offset is a scalar.
-template <int P>
-__device__ __forceinline__ float4 cb_load(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int g) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-        rs, voff, ((P - 1) * kCopy + g * kLanes) * static_cast<int>(sizeof(float4)), 0);
-    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
-                       __uint_as_float(v[3]));
+// One group (I-th of segment SEG) under register naming NM.  `wt`/`dt` are the step's
+// weight and d; two backpointer bits are shifted into `acc`.
+template <int SEG, bool WEIGHTED, int NM, int I>
+__device__ __forceinline__ void acs_group(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+                                          __amdgpu_buffer_rsrc_t rs, uint32_t voff, float wt,
+                                          float dt, uint32_t &acc) {
+    constexpr int P = seg_step(SEG);
+    constexpr int k = 16 * SEG + I;
+    constexpr uint32_t g = seg_group(SEG, I);
+    // at most kPrefetch codebook loads in flight: later loads stay below this point
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    const float4 c = ring[k % kPrefetch];
+    ring[k % kPrefetch] = cb_load_pos<k + kPrefetch>(rs, voff);
+    constexpr int r0 = phys(NM, group_reg(P, g, 0)), r1 = phys(NM, group_reg(P, g, 1));
+    constexpr int r2 = phys(NM, group_reg(P, g, 2)), r3 = phys(NM, group_reg(P, g, 3));
+    const uint32_t u0 = J[r0], u1 = J[r1], u2 = J[r2], u3 = J[r3];
+    const uint32_t m01 = u0 < u1 ? u0 : u1;
+    const uint32_t m23 = u2 < u3 ? u2 : u3;
+    const uint32_t mu = m01 < m23 ? m01 : m23;
+    const uint64_t c01 = __ballot(u1 < u0);
+    const uint64_t c23 = __ballot(u3 < u2);
+    const uint64_t chi = __ballot(m23 < m01);
+    const uint64_t b0 = (chi & c23) | (~chi & c01);
+    acc = shift_in(shift_in(acc, chi), b0);
+    const float m = __uint_as_float(mu);
+    const float e0 = wt - c.x, e1 = wt - c.y, e2 = wt - c.z, e3 = wt - c.w;
+    J[r0] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e0 : e0, e0, m));
+    J[r1] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e1 : e1, e1, m));
+    J[r2] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e2 : e2, e2, m));
+    J[r3] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e3 : e3, e3, m));
 }
 
-// One trellis step at position P (1..3) of the super-step.  `rs` addresses the wave's
-// part of the codebook copies.
-template <int P, bool WEIGHTED>
-__device__ __forceinline__ void acs_step(uint32_t (&J)[kRegs], __amdgpu_buffer_rsrc_t rs,
-                                         uint32_t voff, float wt, float dt,
-                                         uint2 *__restrict__ bp_out) {
-    float4 ring[kPrefetch];
+template <int SEG, bool WEIGHTED, int NM, int... I>
+__device__ __forceinline__ void acs_segment_impl(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+                                                 __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                                 float wt, float dt, uint32_t *bp_word,
+                                                 std::integer_sequence<int, I...>) {
+    uint32_t acc = 0;
+    (acs_group<SEG, WEIGHTED, NM, I>(J, ring, rs, voff, wt, dt, acc), ...);
+    *bp_word = acc;
+}
+
+// Per-block context shared by the segments and transposition rounds.
+struct Ctx {
+    __amdgpu_buffer_rsrc_t rs;  // wave's part of the codebook copies
+    uint32_t voff;              // 16 * lane
+    const float *wcol;          // the block's T weights
+    const float *dcol;          // the block's T values of d (weighted only)
+    uint32_t *bp;               // lane's backpointer words: + 2 * kThreads * t + half
+    uint32_t wb[2];             // LDS byte bases for round writes
+    uint32_t rb[4];             // LDS byte bases for round reads
+};
+
+template <int SEG, bool WEIGHTED, int NM>
+__device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+                                            const Ctx &cx, int t0) {
+    constexpr int P = seg_step(SEG);
+    const int t = t0 + P - 1;  // 0-based step index
+    acs_segment_impl<SEG, WEIGHTED, NM>(J, ring, cx.rs, cx.voff, cx.wcol[t],
+                                        WEIGHTED ? cx.dcol[t] : 1.0f,
+                                        cx.bp + 2 * kThreads * t + seg_half(SEG),
+                                        std::make_integer_sequence<int, 16>{});
+}
+
+extern __shared__ uint32_t lds_stage[];
+
+__device__ __forceinline__ void lds_put(uint32_t base, uint32_t off, uint32_t v) {
+    *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(lds_stage) + base + off) = v;
+}
+__device__ __forceinline__ uint32_t lds_get(uint32_t base, uint32_t off) {
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lds_stage) + base +
+                                               off);
+}
+
+// Transposition rounds (l16_layout.h).  Round RHO writes the logical registers with
+// r[6] = RHO of naming NM and reads the logical registers with r'[0] = RHO of naming
+// 1 - NM; both touch the same physical registers.
+template <int NM, int RHO>
+__device__ __forceinline__ void round_write(const uint32_t (&J)[kRegs], const Ctx &cx) {
 #pragma unroll
-    for (int g = 0; g < kPrefetch; ++g) ring[g] = cb_load<P>(rs, voff, g);
-    uint32_t acc0 = 0, acc1 = 0;
-#pragma unroll
-    for (int g = 0; g < kGroupsPerLane; ++g) {
-        // keep at most kPrefetch codebook loads in flight: later loads stay below this
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" ::: "memory");
-        const float4 c = ring[g % kPrefetch];
-        if (g + kPrefetch < kGroupsPerLane) ring[g % kPrefetch] = cb_load<P>(rs, voff, g + kPrefetch);
-        const int r0 = group_reg(P, g, 0), r1 = group_reg(P, g, 1);
-        const int r2 = group_reg(P, g, 2), r3 = group_reg(P, g, 3);
-        const uint32_t u0 = J[r0], u1 = J[r1], u2 = J[r2], u3 = J[r3];
-        const uint32_t m01 = u0 < u1 ? u0 : u1;
-        const uint32_t m23 = u2 < u3 ? u2 : u3;
-        const uint32_t mu = m01 < m23 ? m01 : m23;
-        const uint64_t c01 = __ballot(u1 < u0);
-        const uint64_t c23 = __ballot(u3 < u2);
-        const uint64_t chi = __ballot(m23 < m01);
-        const uint64_t b0 = (chi & c23) | (~chi & c01);
-        uint32_t &acc = (g < 16) ? acc0 : acc1;
-        acc = shift_in(shift_in(acc, chi), b0);
-        const float m = __uint_as_float(mu);
-        const float e0 = wt - c.x, e1 = wt - c.y, e2 = wt - c.z, e3 = wt - c.w;
-        J[r0] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e0 : e0, e0, m));
-        J[r1] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e1 : e1, e1, m));
-        J[r2] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e2 : e2, e2, m));
-        J[r3] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e3 : e3, e3, m));
+    for (int i = 0; i < 64; ++i) {
+        const uint32_t r = 64u * RHO + i;
+        const uint32_t off = 4u * lds_write_reg(r);
+        lds_put(cx.wb[bit(r, 4)], off - bit(r, 4) * 4u * 2112u * 8u, J[phys(NM, r)]);
     }
-    *bp_out = make_uint2(acc0, acc1);
+}
+template <int NM, int RHO>
+__device__ __forceinline__ void round_read(uint32_t (&J)[kRegs], const Ctx &cx) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        const uint32_t r = 2u * i + RHO;
+        const uint32_t off = 4u * lds_read_reg(r);
+        const uint32_t k = off / (4u * 2112u * 4u);
+        J[phys(1 - NM, r)] = lds_get(cx.rb[k], off - k * 4u * 2112u * 4u);
+    }
 }
 
-// Re-lay the costs out for the next super-step (two LDS rounds split on r[6]).
-__device__ __forceinline__ void transpose(uint32_t (&J)[kRegs], uint32_t *__restrict__ lds,
-                                          uint32_t wlane, uint32_t rlane) {
-    uint32_t Jn[kRegs];
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 64; ++r) lds[wlane + lds_write_reg(r)] = J[r];
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kRegs; r += 2) Jn[r] = lds[rlane + lds_read_reg(r)];
-    __syncthreads();
-#pragma unroll
-    for (int r = 64; r < kRegs; ++r) lds[wlane + lds_write_reg(r)] = J[r];
-    __syncthreads();
-#pragma unroll
-    for (int r = 1; r < kRegs; r += 2) Jn[r] = lds[rlane + lds_read_reg(r)];
-#pragma unroll
-    for (int r = 0; r < kRegs; ++r) J[r] = Jn[r];
+// Super-step (steps t0+1 .. t0+3) under naming NM.  On entry round 1 of the previous
+// transposition is still in LDS (the even registers already hold round 0); on exit the
+// costs have been transposed again for naming 1 - NM, with round 1 left in LDS.
+template <bool WEIGHTED, int NM>
+__device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+                                           const Ctx &cx, int t0) {
+    acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0);
+    acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0);
+    __syncthreads();  // round-1 values written by every wave
+    round_read<1 - NM, 1>(J, cx);
+    acs_segment<2, WEIGHTED, NM>(J, ring, cx, t0);
+    acs_segment<3, WEIGHTED, NM>(J, ring, cx, t0);
+    acs_segment<4, WEIGHTED, NM>(J, ring, cx, t0);
+    __syncthreads();  // every wave has read round 1
+    round_write<NM, 0>(J, cx);
+    acs_segment<5, WEIGHTED, NM>(J, ring, cx, t0);
+    __syncthreads();  // round-0 values written by every wave
+    round_read<NM, 0>(J, cx);
+    __syncthreads();  // every wave has read round 0
+    round_write<NM, 1>(J, cx);
 }
 
-template <int P>
+// The last R = 1 or 2 steps (segments 0..3 in order; for one step the ring is refilled
+// where the order departs from a full super-step).
+template <bool WEIGHTED, int NM, int R>
+__device__ __forceinline__ void tail_steps(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+                                           const Ctx &cx, int t0) {
+    acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0);
+    if constexpr (R == 2) acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0);
+    __syncthreads();
+    round_read<1 - NM, 1>(J, cx);
+    if constexpr (R == 1) ring_fill<32>(ring, cx.rs, cx.voff);
+    acs_segment<2, WEIGHTED, NM>(J, ring, cx, t0);
+    if constexpr (R == 2) acs_segment<3, WEIGHTED, NM>(J, ring, cx, t0);
+}
+
+template <int P, int NM>
 __device__ __forceinline__ void lane_argmin(const uint32_t (&J)[kRegs], uint32_t w,
                                             uint32_t l, uint32_t &bv, uint32_t &bi) {
     // the state of slot (w, l, r) is the OR of a lane/wave part and a register part
@@ -131,7 +235,7 @@ __device__ __forceinline__ void lane_argmin(const uint32_t (&J)[kRegs], uint32_t
 #pragma unroll
     for (int r = 0; r < kRegs; ++r) {
         const uint32_t s = lanepart | state_of(P, 0, 0, r);
-        const uint32_t v = J[r];
+        const uint32_t v = J[phys(NM, r)];
         if (v < bv || (v == bv && s < bi)) {
             bv = v;
             bi = s;
@@ -145,7 +249,6 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     const float4 *__restrict__ cb, int n, int64_t blocks_per_row, int64_t block0,
     uint2 *__restrict__ bp, int64_t bp_per_block, uint32_t *__restrict__ send,
     float *__restrict__ cost_out) {
-    extern __shared__ uint32_t lds[];
     __shared__ uint32_t red_v[kWaves];
     __shared__ uint32_t red_i[kWaves];
 
@@ -155,48 +258,66 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     const int64_t blk = block0 + blockIdx.x;
     const int64_t row = blk / blocks_per_row;
     const int64_t col = blk % blocks_per_row;
-    const float *wrow = W + row * ldw + col * n;
-    const float *drow = WEIGHTED ? d + col * n : nullptr;
     const uint32_t wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform
+
+    Ctx cx;
+    cx.wcol = W + row * ldw + col * n;
+    cx.dcol = WEIGHTED ? d + col * n : nullptr;
     // CDNA buffer descriptor word 3 (raw dword access), as used for gfx9-family parts
-    const __amdgpu_buffer_rsrc_t cbw = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float4 *>(cb + (wu * kGroupsPerLane) * kLanes), 0,
-        3 * kCopy * static_cast<int>(sizeof(float4)), 0x00020000);
-    const uint32_t cbvoff = l * static_cast<uint32_t>(sizeof(float4));
-    uint2 *bpl = bp + blockIdx.x * bp_per_block + (w * kLanes + l);
-    const uint32_t wlane = lds_write_lane(w, l);
-    const uint32_t rlane = lds_read_lane(w, l);
+    cx.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float4 *>(cb + (wu * kGroupsPerLane) * kLanes),
+                                              0, 3 * kCopy * static_cast<int>(sizeof(float4)),
+                                              0x00020000);
+    cx.voff = l * static_cast<uint32_t>(sizeof(float4));
+    cx.bp = reinterpret_cast<uint32_t *>(bp + blockIdx.x * bp_per_block + (w * kLanes + l));
+    // LDS bases, kept opaque so that every access is base + 16-bit immediate
+    const uint32_t wlane = 4u * lds_write_lane(w, l);
+    const uint32_t rlane = 4u * lds_read_lane(w, l);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        cx.wb[k] = wlane + k * 4u * 2112u * 8u;
+        asm volatile("" : "+v"(cx.wb[k]));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        cx.rb[k] = rlane + k * 4u * 2112u * 4u;
+        asm volatile("" : "+v"(cx.rb[k]));
+    }
 
     uint32_t J[kRegs];  // fp32 costs held as their bit patterns
 #pragma unroll
     for (int r = 0; r < kRegs; ++r) J[r] = 0u;
+    float4 ring[kPrefetch];
+    ring_fill<0>(ring, cx.rs, cx.voff);
 
+    // Every super-step ends with a transposition whose second round is read at the start
+    // of the next one; the all-zero start is staged the same way, so all super-steps run
+    // the same branch-free code.  Super-steps alternate between namings 1 and 0 so that
+    // the last one runs under naming 1 and the tail under naming 0.
+#pragma unroll
+    for (int r = 0; r < kRegs; ++r) asm volatile("" : "+v"(J[r]));  // keep the zeros opaque
+    round_write<1, 1>(J, cx);
     const int Q = n / 3;
     const int R = n % 3;
-    int t = 0;
-    for (int q = 0; q < Q; ++q) {
-        acs_step<1, WEIGHTED>(J, cbw, cbvoff, wrow[t], WEIGHTED ? drow[t] : 1.0f, bpl + t * kThreads);
-        acs_step<2, WEIGHTED>(J, cbw, cbvoff, wrow[t + 1], WEIGHTED ? drow[t + 1] : 1.0f,
-                              bpl + (t + 1) * kThreads);
-        acs_step<3, WEIGHTED>(J, cbw, cbvoff, wrow[t + 2], WEIGHTED ? drow[t + 2] : 1.0f,
-                              bpl + (t + 2) * kThreads);
-        t += 3;
-        if (t < n) transpose(J, lds, wlane, rlane);
+    if (Q & 1) super_step<WEIGHTED, 1>(J, ring, cx, 0);
+    for (int q = Q & 1; q < Q; q += 2) {
+        super_step<WEIGHTED, 0>(J, ring, cx, 3 * q);
+        super_step<WEIGHTED, 1>(J, ring, cx, 3 * q + 3);
     }
-    if (R >= 1)
-        acs_step<1, WEIGHTED>(J, cbw, cbvoff, wrow[t], WEIGHTED ? drow[t] : 1.0f, bpl + t * kThreads);
-    if (R >= 2)
-        acs_step<2, WEIGHTED>(J, cbw, cbvoff, wrow[t + 1], WEIGHTED ? drow[t + 1] : 1.0f,
-                              bpl + (t + 1) * kThreads);
+    if (R == 1) {
+        tail_steps<WEIGHTED, 0, 1>(J, ring, cx, 3 * Q);
+    } else if (R == 2) {
+        tail_steps<WEIGHTED, 0, 2>(J, ring, cx, 3 * Q);
+    } else {
+        __syncthreads();  // collect the last round
+        round_read<1, 1>(J, cx);
+    }
 
     uint32_t bv = 0xFFFFFFFFu;  // above every finite or infinite cost pattern
     uint32_t bi = 0xFFFFFFFFu;
-    if (R == 1)
-        lane_argmin<1>(J, w, l, bv, bi);
-    else if (R == 2)
-        lane_argmin<2>(J, w, l, bv, bi);
-    else
-        lane_argmin<3>(J, w, l, bv, bi);
+    // final layout: step R of a super-step (R = 0: its start) under naming 0
+    if (R == 1) lane_argmin<1, 0>(J, w, l, bv, bi);
+    else if (R == 2) lane_argmin<2, 0>(J, w, l, bv, bi);
+    else lane_argmin<0, 0>(J, w, l, bv, bi);
     for (int off = 32; off >= 1; off >>= 1) {
         const uint32_t ov = __shfl_xor(bv, off);
         const uint32_t oi = __shfl_xor(bi, off);
@@ -239,8 +360,8 @@ __global__ __launch_bounds__(64) void traceback_l16_kernel(
             const Slot sl = slot_of(p, s);
             const uint32_t g = reg_group(p, sl.r);
             const uint2 word = bpb[(t - 1) * kThreads + sl.w * kLanes + sl.l];
-            const uint32_t bits = (g < 16) ? word.x : word.y;
-            const uint32_t jb = (bits >> (2 * (15 - (g & 15)))) & 3u;
+            const uint32_t bits = bp_half(p, g) ? word.y : word.x;
+            const uint32_t jb = (bits >> bp_shift(p, g)) & 3u;
             chunk[t - 1] = static_cast<uint8_t>(s & 3u);
             s = (jb << 14) | (s >> 2);
         }

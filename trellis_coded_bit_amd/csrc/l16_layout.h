@@ -88,6 +88,41 @@ __host__ __device__ constexpr uint32_t reg_group(int p, uint32_t r) {
     return (r & ((1u << a) - 1u)) | ((r >> (a + 2)) << a);
 }
 
+// Processing order of a super-step: six segments of 16 groups each.  Splitting steps
+// 1 and 2 by the parity of g (= bit 0 of the register, = the LDS round of the
+// preceding transposition) lets half the trellis advance two steps while the other
+// half is still in transit; step 3 is split by g < 16 (= r[6], the round of the
+// following transposition) so the first half can be written out early.
+//   segment : 0      1      2      3      4      5
+//   step    : 1      2      1      2      3      3
+//   groups  : even   even   odd    odd    0..15  16..31
+__host__ __device__ constexpr int seg_step(int seg) {
+    return (seg == 0 || seg == 2) ? 1 : ((seg == 1 || seg == 3) ? 2 : 3);
+}
+__host__ __device__ constexpr int seg_half(int seg) {
+    return (seg == 0 || seg == 1 || seg == 4) ? 0 : 1;
+}
+// i-th group (i = 0..15) of a segment
+__host__ __device__ constexpr uint32_t seg_group(int seg, int i) {
+    return seg_step(seg) == 3 ? 16u * seg_half(seg) + i : 2u * i + seg_half(seg);
+}
+// Backpointer word of step p: per lane two 32-bit words (halves), 2 bits per group,
+// the segment's first group in the top bits.
+__host__ __device__ constexpr uint32_t bp_half(int p, uint32_t g) {
+    return p == 3 ? (g >> 4) : (g & 1u);
+}
+__host__ __device__ constexpr uint32_t bp_shift(int p, uint32_t g) {
+    return 2u * (15u - (p == 3 ? (g & 15u) : (g >> 1)));
+}
+
+// Register naming.  Odd super-steps keep logical register r in physical register
+// phys(1, r) = r with bits 0 and 6 swapped.  A transposition round then refills exactly
+// the physical registers it has just written out: round 0 moves logical r[6] = 0 into
+// logical r'[0] = 0, and phys(m, {r[6] = 0}) = phys(1 - m, {r'[0] = 0}) for m = 0, 1.
+__host__ __device__ constexpr uint32_t phys(int naming, uint32_t r) {
+    return naming ? ((r & 0x3Eu) | (bit(r, 0) << 6) | bit(r, 6)) : r;
+}
+
 // Destination of the value in slot (w, l, r) at the end of a super-step (p = 3).
 __host__ __device__ constexpr Slot transpose_dest(uint32_t w, uint32_t l, uint32_t r) {
     const uint32_t rn = bit(r, 6) | (bit(l, 5) << 1) | (bit(w, 1) << 2) | (bit(w, 2) << 3) |
