@@ -65,6 +65,26 @@ def log(msg, quiet=False):
         sys.stderr.flush()
 
 
+def measured_traffic(workload_name):
+    """HBM bytes per forward launch from the committed rocprofv3 counters, if they were
+    taken on the kernel sources as they are now (else None)."""
+    import hashlib
+    for fn in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        if not fn.endswith(".counters.json"):
+            continue
+        with open(os.path.join(ROOT, "profiles", fn)) as f:
+            rec = json.load(f)
+        if rec.get("workload") != workload_name:
+            continue
+        h = hashlib.sha256()
+        for src in rec["kernel_sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() == rec["kernel_source_sha256"]:
+            return rec["hbm_bytes_per_dispatch"]
+    return None
+
+
 def cpu_baseline(w, W, d, C, nblocks, threads):
     import oracle
     rng = np.random.default_rng(12345)
@@ -175,7 +195,8 @@ def main():
                    "T": w.T, "d": "weighted (LDL diagonal)" if d is not None else "1 (NULL)",
                    "codebook": f"2^{w.L} shuffled Gaussian quantiles, seed {w.codebook_seed}"},
         "roofline": {"bound": "alu", "achieved": achieved_tops, "peak": peak_tops,
-                     "unit": "TOP/s", "frac": achieved_tops / peak_tops, "traffic": None},
+                     "unit": "TOP/s", "frac": achieved_tops / peak_tops,
+                     "traffic": measured_traffic(w.name)},
         "acs": {"kernel_ms": acs_ms, "state_updates_per_s": acs_ops_per_s,
                 "valu_ops_per_update": ops, "valu_pct": 100.0 * achieved_tops / peak_tops,
                 "bp_write_GBps": bp_gbps, "bp_pct_hbm": 100.0 * bp_gbps / HBM_PEAK_GBPS,
