@@ -143,6 +143,58 @@ int main() {
             CHECK(out == in && out.size() == 64);
         }
     for (uint32_t r = 0; r < 128; ++r) CHECK(phys(1, phys(1, r)) == r && phys(0, r) == r);
+    // k*V = 3: bijection, group structure (8 predecessors (j << 13) | x, successors
+    // (x << 3) | b), transposition after two steps, segments and backpointer slots
+    for (int p = 0; p <= 2; ++p) {
+        std::vector<int> seen(1 << 16, 0);
+        for (uint32_t w = 0; w < 8; ++w)
+            for (uint32_t l = 0; l < 64; ++l)
+                for (uint32_t r = 0; r < 128; ++r) {
+                    uint32_t st = state_of3(p, w, l, r);
+                    seen[st]++;
+                    Slot q = slot_of3(p, st);
+                    CHECK(q.w == w && q.l == l && q.r == r);
+                }
+        for (int st = 0; st < (1 << 16); ++st) CHECK(seen[st] == 1);
+    }
+    for (int p = 1; p <= 2; ++p)
+        for (uint32_t w = 0; w < 8; ++w)
+            for (uint32_t l = 0; l < 64; ++l)
+                for (uint32_t g = 0; g < 16; ++g) {
+                    uint32_t x = state_of3(p - 1, w, l, group_reg3(p, g, 0)) & 0x1FFFu;
+                    for (uint32_t j = 0; j < 8; ++j) {
+                        uint32_t r = group_reg3(p, g, j);
+                        CHECK(r < 128 && reg_group3(p, r) == g);
+                        CHECK(state_of3(p - 1, w, l, r) == ((j << 13) | x));
+                        CHECK(state_of3(p, w, l, r) == ((x << 3) | j));
+                    }
+                }
+    for (uint32_t w = 0; w < 8; ++w)
+        for (uint32_t l = 0; l < 64; ++l)
+            for (uint32_t r = 0; r < 128; ++r) {
+                Slot d = transpose_dest(w, l, r);
+                CHECK(state_of3(2, w, l, r) == state_of3(0, d.w, d.l, d.r));
+            }
+    for (int p = 1; p <= 2; ++p) {
+        std::set<uint32_t> gs, slots;
+        for (int seg = 0; seg < 4; ++seg) {
+            if (seg3_step(seg) != p) continue;
+            for (int i = 0; i < 8; ++i) {
+                uint32_t g = seg3_group(seg, i);
+                CHECK(g < 16);
+                gs.insert(g);
+                CHECK(bp3_half(p, g) == (uint32_t)seg3_half(seg));
+                CHECK(bp3_shift(p, g) == 3u * (7u - (uint32_t)i));
+                slots.insert(bp3_half(p, g) * 32 + bp3_shift(p, g));
+                for (uint32_t b = 0; b < 8; ++b) {
+                    uint32_t r = group_reg3(p, g, b);
+                    if (p == 1) CHECK((r & 1u) == (uint32_t)seg3_half(seg));
+                    else CHECK(((r >> 6) & 1u) == (uint32_t)seg3_half(seg));
+                }
+            }
+        }
+        CHECK(gs.size() == 16 && slots.size() == 16);
+    }
     if (fails) {
         std::printf("%d failures\n", fails);
         return 1;

@@ -65,7 +65,14 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("L,k,V,T,M,N,weighted", SMALL)
+# L = 16 register-resident kernels: every combination of super-step count parity and
+# leftover steps (k*V = 2: three steps per super-step; k*V = 3: two)
+L16_EDGES = [(16, 2, 1, n, 2, 2 * n, n % 2 == 0) for n in range(1, 13)] + \
+            [(16, 3, 1, n, 2, 2 * n, n % 2 == 1) for n in range(1, 9)] + \
+            [(16, 3, 1, 256, 3, 768, True), (16, 3, 1, 255, 1, 510, False)]
+
+
+@pytest.mark.parametrize("L,k,V,T,M,N,weighted", SMALL + L16_EDGES)
 def test_parity_small(oracle_lib, L, k, V, T, M, N, weighted):
     _say(f"case L={L} k={k} V={V} T={T} M={M} N={N} weighted={weighted}")
     W, d = wl.random_small(1000 * L + 10 * k + V + T, M, N, weighted)

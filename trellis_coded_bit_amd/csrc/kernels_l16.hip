@@ -15,6 +15,7 @@
 // from an L2-resident 768 KiB array.
 #include <hip/hip_runtime.h>
 
+#include "l16_device.h"
 #include "l16_layout.h"
 #include "tcq.h"
 #include "tcq_internal.h"
@@ -26,8 +27,6 @@ namespace {
 
 using namespace l16;
 
-constexpr int kThreads = kWaves * kLanes;  // 512
-constexpr int kCopy = kWaves * kGroupsPerLane * kLanes;  // float4 entries per copy
 constexpr int kPrefetch = 12;                           // groups of codebook in flight
 
 __global__ __launch_bounds__(256) void l16_prepare_kernel(const float *__restrict__ C,
@@ -61,6 +60,9 @@ __device__ __forceinline__ float4 cb_load(__amdgpu_buffer_rsrc_t rs, uint32_t vo
 // (position k = 16 * segment + i, 96 per super-step); a ring of kPrefetch loads runs
 // ahead of the consumer, across segment and super-step boundaries.
 constexpr int kPositions = 96;
+// the ring runs across super-steps: position k lives in slot k mod kPrefetch in every
+// super-step only if the ring size divides the positions per super-step
+static_assert(kPositions % kPrefetch == 0, "ring size must divide a super-step");
 
 template <int K>
 __device__ __forceinline__ float4 cb_load_pos(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
@@ -79,14 +81,6 @@ template <int K0>
 __device__ __forceinline__ void ring_fill(float4 (&ring)[kPrefetch], __amdgpu_buffer_rsrc_t rs,
                                           uint32_t voff) {
     ring_prime<K0>(ring, rs, voff, std::make_integer_sequence<int, kPrefetch>{});
-}
-
-// Shift one bit per lane, taken from a wave-wide compare mask, into acc:
-// acc = 2 * acc + mask[lane] in a single VALU op (carry-in from an SGPR pair).
-__device__ __forceinline__ uint32_t shift_in(uint32_t acc, uint64_t mask) {
-    uint32_t r;
-    asm volatile("v_addc_co_u32 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(acc), "s"(mask) : "vcc");
-    return r;
 }
 
 // Path costs are non-negative floats (sums of d * e * e >= 0 starting from +0, never
@@ -136,17 +130,6 @@ __device__ __forceinline__ void acs_segment_impl(uint32_t (&J)[kRegs], float4 (&
     *bp_word = acc;
 }
 
-// Per-block context shared by the segments and transposition rounds.
-struct Ctx {
-    __amdgpu_buffer_rsrc_t rs;  // wave's part of the codebook copies
-    uint32_t voff;              // 16 * lane
-    const float *wcol;          // the block's T weights
-    const float *dcol;          // the block's T values of d (weighted only)
-    uint32_t *bp;               // lane's backpointer words: + 2 * kThreads * t + half
-    uint32_t wb[2];             // LDS byte bases for round writes
-    uint32_t rb[4];             // LDS byte bases for round reads
-};
-
 template <int SEG, bool WEIGHTED, int NM>
 __device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
                                             const Ctx &cx, int t0) {
@@ -156,39 +139,6 @@ __device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)
                                         WEIGHTED ? cx.dcol[t] : 1.0f,
                                         cx.bp + 2 * kThreads * t + seg_half(SEG),
                                         std::make_integer_sequence<int, 16>{});
-}
-
-extern __shared__ uint32_t lds_stage[];
-
-__device__ __forceinline__ void lds_put(uint32_t base, uint32_t off, uint32_t v) {
-    *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(lds_stage) + base + off) = v;
-}
-__device__ __forceinline__ uint32_t lds_get(uint32_t base, uint32_t off) {
-    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lds_stage) + base +
-                                               off);
-}
-
-// Transposition rounds (l16_layout.h).  Round RHO writes the logical registers with
-// r[6] = RHO of naming NM and reads the logical registers with r'[0] = RHO of naming
-// 1 - NM; both touch the same physical registers.
-template <int NM, int RHO>
-__device__ __forceinline__ void round_write(const uint32_t (&J)[kRegs], const Ctx &cx) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-        const uint32_t r = 64u * RHO + i;
-        const uint32_t off = 4u * lds_write_reg(r);
-        lds_put(cx.wb[bit(r, 4)], off - bit(r, 4) * 4u * 2112u * 8u, J[phys(NM, r)]);
-    }
-}
-template <int NM, int RHO>
-__device__ __forceinline__ void round_read(uint32_t (&J)[kRegs], const Ctx &cx) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-        const uint32_t r = 2u * i + RHO;
-        const uint32_t off = 4u * lds_read_reg(r);
-        const uint32_t k = off / (4u * 2112u * 4u);
-        J[phys(1 - NM, r)] = lds_get(cx.rb[k], off - k * 4u * 2112u * 4u);
-    }
 }
 
 // Super-step (steps t0+1 .. t0+3) under naming NM.  On entry round 1 of the previous
@@ -249,39 +199,15 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     const float4 *__restrict__ cb, int n, int64_t blocks_per_row, int64_t block0,
     uint2 *__restrict__ bp, int64_t bp_per_block, uint32_t *__restrict__ send,
     float *__restrict__ cost_out) {
-    __shared__ uint32_t red_v[kWaves];
-    __shared__ uint32_t red_i[kWaves];
-
     const uint32_t tid = threadIdx.x;
     const uint32_t w = tid >> 6;
     const uint32_t l = tid & 63;
     const int64_t blk = block0 + blockIdx.x;
     const int64_t row = blk / blocks_per_row;
     const int64_t col = blk % blocks_per_row;
-    const uint32_t wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform
 
-    Ctx cx;
-    cx.wcol = W + row * ldw + col * n;
-    cx.dcol = WEIGHTED ? d + col * n : nullptr;
-    // CDNA buffer descriptor word 3 (raw dword access), as used for gfx9-family parts
-    cx.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float4 *>(cb + (wu * kGroupsPerLane) * kLanes),
-                                              0, 3 * kCopy * static_cast<int>(sizeof(float4)),
-                                              0x00020000);
-    cx.voff = l * static_cast<uint32_t>(sizeof(float4));
-    cx.bp = reinterpret_cast<uint32_t *>(bp + blockIdx.x * bp_per_block + (w * kLanes + l));
-    // LDS bases, kept opaque so that every access is base + 16-bit immediate
-    const uint32_t wlane = 4u * lds_write_lane(w, l);
-    const uint32_t rlane = 4u * lds_read_lane(w, l);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        cx.wb[k] = wlane + k * 4u * 2112u * 8u;
-        asm volatile("" : "+v"(cx.wb[k]));
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        cx.rb[k] = rlane + k * 4u * 2112u * 4u;
-        asm volatile("" : "+v"(cx.rb[k]));
-    }
+    const Ctx cx = make_ctx(W, ldw, WEIGHTED ? d : nullptr, cb, n, row, col, w, l,
+                            bp + blockIdx.x * bp_per_block);
 
     uint32_t J[kRegs];  // fp32 costs held as their bit patterns
 #pragma unroll
@@ -318,29 +244,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     if (R == 1) lane_argmin<1, 0>(J, w, l, bv, bi);
     else if (R == 2) lane_argmin<2, 0>(J, w, l, bv, bi);
     else lane_argmin<0, 0>(J, w, l, bv, bi);
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t ov = __shfl_xor(bv, off);
-        const uint32_t oi = __shfl_xor(bi, off);
-        if (ov < bv || (ov == bv && oi < bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
-    if (l == 0) {
-        red_v[w] = bv;
-        red_i[w] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        for (int k = 1; k < kWaves; ++k) {
-            if (red_v[k] < bv || (red_v[k] == bv && red_i[k] < bi)) {
-                bv = red_v[k];
-                bi = red_i[k];
-            }
-        }
-        send[blockIdx.x] = bi;
-        cost_out[blk] = __uint_as_float(bv);
-    }
+    block_select(bv, bi, w, l, send + blockIdx.x, cost_out + blk);
 }
 
 // One wave per block: follow the remembered predecessors back from the end state and

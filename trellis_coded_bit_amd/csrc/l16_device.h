@@ -1,0 +1,134 @@
+// Device helpers shared by the L = 16 forward kernels (k*V = 2 and 3): the per-block
+// context, the carry shift-in of compare masks, and the two LDS rounds of the
+// transposition (layout in l16_layout.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "l16_layout.h"
+
+namespace tcq {
+namespace l16 {
+
+constexpr int kThreads = kWaves * kLanes;                // 512
+constexpr int kCopy = kWaves * kGroupsPerLane * kLanes;  // float4 entries per codebook copy
+
+// Shift one bit per lane, taken from a wave-wide compare mask, into acc:
+// acc = 2 * acc + mask[lane] in a single VALU op (carry-in from an SGPR pair).
+__device__ __forceinline__ uint32_t shift_in(uint32_t acc, uint64_t mask) {
+    uint32_t r;
+    asm volatile("v_addc_co_u32 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(acc), "s"(mask) : "vcc");
+    return r;
+}
+
+// Per-block context shared by the segments and transposition rounds.
+struct Ctx {
+    __amdgpu_buffer_rsrc_t rs;  // wave's part of the codebook copies
+    uint32_t voff;              // 16 * lane
+    const float *wcol;          // the block's T weights
+    const float *dcol;          // the block's T values of d (weighted only)
+    uint32_t *bp;               // lane's backpointer words: + 2 * kThreads * t + half
+    uint32_t wb[2];             // LDS byte bases for round writes
+    uint32_t rb[4];             // LDS byte bases for round reads
+};
+
+// Context of one coding block (row, col) for lane l of wave w.  The codebook copies
+// start at cb; each wave addresses its own 2048-entry slice of every copy through a
+// raw buffer descriptor, so every load is (16 * lane) + scalar offset + immediate.
+__device__ __forceinline__ Ctx make_ctx(const float *W, int64_t ldw, const float *d,
+                                        const float4 *cb, int n, int64_t row, int64_t col,
+                                        uint32_t w, uint32_t l, uint2 *bp_block) {
+    Ctx cx;
+    const uint32_t wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform
+    cx.wcol = W + row * ldw + col * n;
+    cx.dcol = d ? d + col * n : nullptr;
+    // CDNA buffer descriptor word 3 (raw dword access), as used for gfx9-family parts
+    cx.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float4 *>(cb + wu * (kCopy / kWaves)),
+                                              0, 3 * kCopy * static_cast<int>(sizeof(float4)),
+                                              0x00020000);
+    cx.voff = l * static_cast<uint32_t>(sizeof(float4));
+    cx.bp = reinterpret_cast<uint32_t *>(bp_block + (w * kLanes + l));
+    // LDS bases, kept opaque so that every access is base + 16-bit immediate
+    const uint32_t wlane = 4u * lds_write_lane(w, l);
+    const uint32_t rlane = 4u * lds_read_lane(w, l);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        cx.wb[k] = wlane + k * 4u * 2112u * 8u;
+        asm volatile("" : "+v"(cx.wb[k]));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        cx.rb[k] = rlane + k * 4u * 2112u * 4u;
+        asm volatile("" : "+v"(cx.rb[k]));
+    }
+    return cx;
+}
+
+extern __shared__ uint32_t lds_stage[];
+
+__device__ __forceinline__ void lds_put(uint32_t base, uint32_t off, uint32_t v) {
+    *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(lds_stage) + base + off) = v;
+}
+__device__ __forceinline__ uint32_t lds_get(uint32_t base, uint32_t off) {
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lds_stage) + base +
+                                               off);
+}
+
+// Transposition rounds (l16_layout.h).  Round RHO writes the logical registers with
+// r[6] = RHO of naming NM and reads the logical registers with r'[0] = RHO of naming
+// 1 - NM; both touch the same physical registers.
+template <int NM, int RHO>
+__device__ __forceinline__ void round_write(const uint32_t (&J)[kRegs], const Ctx &cx) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        const uint32_t r = 64u * RHO + i;
+        const uint32_t off = 4u * lds_write_reg(r);
+        lds_put(cx.wb[bit(r, 4)], off - bit(r, 4) * 4u * 2112u * 8u, J[phys(NM, r)]);
+    }
+}
+template <int NM, int RHO>
+__device__ __forceinline__ void round_read(uint32_t (&J)[kRegs], const Ctx &cx) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        const uint32_t r = 2u * i + RHO;
+        const uint32_t off = 4u * lds_read_reg(r);
+        const uint32_t k = off / (4u * 2112u * 4u);
+        J[phys(1 - NM, r)] = lds_get(cx.rb[k], off - k * 4u * 2112u * 4u);
+    }
+}
+
+// Lowest-index minimum over the workgroup: (bv, bi) are each lane's best cost pattern
+// and state; lane 0 of wave 0 writes the chosen end state and its cost.
+__device__ __forceinline__ void block_select(uint32_t bv, uint32_t bi, uint32_t w, uint32_t l,
+                                             uint32_t *send_slot, float *cost_slot) {
+    __shared__ uint32_t red_v[kWaves];
+    __shared__ uint32_t red_i[kWaves];
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t ov = __shfl_xor(bv, off);
+        const uint32_t oi = __shfl_xor(bi, off);
+        if (ov < bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    if (l == 0) {
+        red_v[w] = bv;
+        red_i[w] = bi;
+    }
+    __syncthreads();
+    if (w == 0 && l == 0) {
+        for (int k = 1; k < kWaves; ++k) {
+            if (red_v[k] < bv || (red_v[k] == bv && red_i[k] < bi)) {
+                bv = red_v[k];
+                bi = red_i[k];
+            }
+        }
+        *send_slot = bi;
+        *cost_slot = __uint_as_float(bv);
+    }
+}
+
+}  // namespace l16
+}  // namespace tcq

@@ -88,6 +88,56 @@ __host__ __device__ constexpr uint32_t reg_group(int p, uint32_t r) {
     return (r & ((1u << a) - 1u)) | ((r >> (a + 2)) << a);
 }
 
+// ---------------------------------------------------------------------------------
+// k*V = 3.  A super-step is two steps of three bits; the six register bits r[5:0]
+// still hold the oldest six state bits at its start, so the layout above, the
+// transposition and the LDS staging are unchanged.  After p steps the state is the
+// start-of-super-step state rotated left by 3p bits.  Step 1 replaces r[5:3], step 2
+// r[2:0]; a group is the 8 registers that differ in those bits.
+// ---------------------------------------------------------------------------------
+__host__ __device__ constexpr uint32_t rotl16(uint32_t s, int k) {
+    k &= 15;
+    return ((s << k) | (s >> ((16 - k) & 15))) & 0xFFFFu;
+}
+__host__ __device__ constexpr uint32_t state_of3(int p, uint32_t w, uint32_t l, uint32_t r) {
+    return rotl16(state_of(0, w, l, r), 3 * p);
+}
+__host__ __device__ constexpr Slot slot_of3(int p, uint32_t s) {
+    return slot_of(0, rotl16(s, 16 - ((3 * p) & 15)));
+}
+__host__ __device__ constexpr int active_shift3(int p) { return p == 1 ? 3 : 0; }
+// register of successor b (0..7) of group g (0..15) at step p; g fills the other four
+// register bits in ascending order
+__host__ __device__ constexpr uint32_t group_reg3(int p, uint32_t g, uint32_t b) {
+    const int a = active_shift3(p);
+    const uint32_t low = g & ((1u << a) - 1u);
+    const uint32_t high = g >> a;
+    return low | (b << a) | (high << (a + 3));
+}
+__host__ __device__ constexpr uint32_t reg_group3(int p, uint32_t r) {
+    const int a = active_shift3(p);
+    return (r & ((1u << a) - 1u)) | ((r >> (a + 3)) << a);
+}
+// Segment order of a k*V = 3 super-step: four segments of 8 groups.
+//   segment : 0      1      2       3
+//   step    : 1      1      2       2
+//   groups  : even   odd    0..7    8..15
+// (step-1 groups split by r[0], the round of the preceding transposition; step-2
+// groups by r[6], the round of the following one)
+__host__ __device__ constexpr int seg3_step(int seg) { return seg < 2 ? 1 : 2; }
+__host__ __device__ constexpr int seg3_half(int seg) { return seg & 1; }
+__host__ __device__ constexpr uint32_t seg3_group(int seg, int i) {
+    return seg < 2 ? 2u * i + (seg & 1) : 8u * (seg & 1) + i;
+}
+// backpointers: per lane and step two 32-bit words, 3 bits per group, the segment's
+// first group in the top bits (bits 31..24 unused)
+__host__ __device__ constexpr uint32_t bp3_half(int p, uint32_t g) {
+    return p == 1 ? (g & 1u) : (g >> 3);
+}
+__host__ __device__ constexpr uint32_t bp3_shift(int p, uint32_t g) {
+    return 3u * (7u - (p == 1 ? (g >> 1) : (g & 7u)));
+}
+
 // Processing order of a super-step: six segments of 16 groups each.  Splitting steps
 // 1 and 2 by the parity of g (= bit 0 of the register, = the LDS round of the
 // preceding transposition) lets half the trellis advance two steps while the other

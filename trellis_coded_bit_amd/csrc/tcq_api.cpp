@@ -35,6 +35,11 @@ Plan plan_for(const Problem &p) {
         pl.fixed = align_up(l16_fixed_bytes(p), 256);
         pl.bp_bytes = align_up(l16_bp_bytes(p), 256);
         pl.cost_bytes = 0;
+    } else if (l16k3_supported(p)) {
+        pl.variant = kL16RegsK3;
+        pl.fixed = align_up(l16k3_fixed_bytes(p), 256);
+        pl.bp_bytes = align_up(l16k3_bp_bytes(p), 256);
+        pl.cost_bytes = 0;
     } else {
         const int64_t nw64 = (p.ngroups + 63) / 64;
         pl.bp_bytes = align_up(static_cast<size_t>(p.n) * p.kv * nw64 * 8, 256);
@@ -186,6 +191,9 @@ static int encode_impl(const char *fn, const float *W, int64_t M, int64_t N, int
     if (pl.variant == kL16Regs) {
         e = launch_l16_prepare(p, codebook, ws, stream);
         if (e != hipSuccess) return hip_fail(fn, "codebook preparation launch", e);
+    } else if (pl.variant == kL16RegsK3) {
+        e = launch_l16k3_prepare(p, codebook, ws, stream);
+        if (e != hipSuccess) return hip_fail(fn, "codebook preparation launch", e);
     }
     for (int64_t b0 = 0; b0 < p.nblocks; b0 += batch) {
         const int64_t nb = (p.nblocks - b0 < batch) ? p.nblocks - b0 : batch;
@@ -201,6 +209,15 @@ static int encode_impl(const char *fn, const float *W, int64_t M, int64_t N, int
                 if (e != hipSuccess) return hip_fail(fn, "hipEventRecord", e);
             }
             e = launch_traceback_l16(p, pl, b0, nb, ws, bitstream, start_state, stream);
+            if (e != hipSuccess) return hip_fail(fn, "traceback launch", e);
+        } else if (pl.variant == kL16RegsK3) {
+            e = launch_acs_l16k3(p, pl, W, d, b0, nb, ws, cost, stream);
+            if (e != hipSuccess) return hip_fail(fn, "ACS launch", e);
+            if (b0 + nb >= p.nblocks && acs_end) {
+                e = hipEventRecord(acs_end, stream);
+                if (e != hipSuccess) return hip_fail(fn, "hipEventRecord", e);
+            }
+            e = launch_traceback_l16k3(p, pl, b0, nb, ws, bitstream, start_state, stream);
             if (e != hipSuccess) return hip_fail(fn, "traceback launch", e);
         } else {
             e = launch_acs_generic(p, pl, W, d, codebook, b0, nb, ws, cost, stream);

@@ -33,7 +33,8 @@ struct Plan {
 enum Variant : int {
     kGenericLds = 0,     // any supported shape, cost vectors double-buffered in LDS
     kGenericGlobal = 1,  // any supported shape, cost vectors in the workspace (L2)
-    kL16Regs = 2,        // L = 16, six active bits per super-step, costs in VGPRs
+    kL16Regs = 2,        // L = 16, k*V = 2, costs in VGPRs (three-step super-steps)
+    kL16RegsK3 = 3,      // L = 16, k*V = 3, costs in VGPRs (two-step super-steps)
 };
 
 Plan plan_for(const Problem &p);
@@ -59,6 +60,18 @@ hipError_t launch_acs_l16(const Problem &p, const Plan &pl, const float *W, cons
 hipError_t launch_traceback_l16(const Problem &p, const Plan &pl, int64_t block0, int64_t nb,
                                 const char *ws, uint32_t *bitstream, uint32_t *start_state,
                                 hipStream_t s);
+
+// L = 16, k*V = 3 register-resident path.
+bool l16k3_supported(const Problem &p);
+size_t l16k3_fixed_bytes(const Problem &p);
+size_t l16k3_bp_bytes(const Problem &p);
+hipError_t launch_l16k3_prepare(const Problem &p, const float *C, char *fixed_ws,
+                                hipStream_t s);
+hipError_t launch_acs_l16k3(const Problem &p, const Plan &pl, const float *W, const float *d,
+                            int64_t block0, int64_t nb, char *ws, float *cost, hipStream_t s);
+hipError_t launch_traceback_l16k3(const Problem &p, const Plan &pl, int64_t block0, int64_t nb,
+                                  const char *ws, uint32_t *bitstream, uint32_t *start_state,
+                                  hipStream_t s);
 
 // Workspace layout helpers: [fixed area][per-block area x batch]
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
