@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--cpu-blocks", type=int, default=1024,
                     help="blocks in the CPU-oracle sample (0: skip)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="0: min(16, cpu count)")
+    ap.add_argument("--gemv-iters", type=int, default=200,
+                    help="calls of the fused decode+GEMV timed after the encoder (0: skip)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES bytes (reference for "
@@ -97,6 +99,35 @@ def cpu_baseline(w, W, d, C, nblocks, threads):
             "sample": f"{blocks.size} seeded-random blocks of the same workload "
                       f"({blocks.size * w.T} weights), one block per thread at a time, "
                       f"{dt:.2f} s wall"}
+
+
+def gemv_bench(torch, _lib, w, enc, Ct, iters):
+    """y = W_hat x on the bitstream the encoder just wrote (batch 1).  Algorithmic bytes:
+    the bitstream, the start states, x and y; the codebook gathers hit the L2 cache."""
+    g = torch.Generator(device="cpu").manual_seed(77)
+    x = torch.randn(w.N, generator=g).to(Ct.device)
+    y = torch.empty(w.M, dtype=torch.float32, device=Ct.device)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        _lib.tcq_decode_gemv(enc.bitstream.data_ptr(), enc.start_state.data_ptr(),
+                             Ct.data_ptr(), w.M, w.N, w.L, w.k, w.V, w.T, x.data_ptr(),
+                             y.data_ptr(), stream.cuda_stream)
+
+    for _ in range(3):
+        call()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(iters):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / iters
+    nbytes = (enc.bitstream.numel() + enc.start_state.numel() + w.N + w.M) * 4
+    gbps = nbytes / (us / 1e6) / 1e9
+    return {"us_per_call": us, "algorithmic_bytes": nbytes, "achieved_GBps": gbps,
+            "frac_hbm": gbps / HBM_PEAK_GBPS, "weights_per_s": w.weights / (us / 1e6)}
 
 
 def main():
@@ -202,6 +233,10 @@ def main():
                 "bp_write_GBps": bp_gbps, "bp_pct_hbm": 100.0 * bp_gbps / HBM_PEAK_GBPS,
                 "share_of_step": acs_ms / ms_per_step},
     }
+    if args.gemv_iters > 0:
+        log(f"[bench] fused decode+GEMV on the encoded matrix, {args.gemv_iters} calls",
+            args.quiet)
+        result["decode_gemv"] = gemv_bench(torch, _lib, w, out, Ct, args.gemv_iters)
     if args.cpu_blocks > 0:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         log(f"[bench] cpu oracle on {args.cpu_blocks} blocks, {threads} threads", args.quiet)

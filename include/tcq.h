@@ -146,6 +146,21 @@ int tcq_decode(const uint32_t *bitstream, const uint32_t *start_state, const flo
                int64_t M, int64_t N, int L, int k, int V, int T, float *out, int64_t ldo,
                hipStream_t stream);
 
+/*
+ * tcq_decode_gemv -- y = W_hat x with W_hat decoded inside the product (Pingala-8 post,
+ * decoding paragraph: decoding is cheap and runs inside the matrix-vector product).
+ *   bitstream, start_state : device, as written by tcq_encode for an M x N problem
+ *   codebook               : device, 2^L * V floats
+ *   x                      : device, N floats
+ *   y                      : device out, M floats; y[r] = sum_c W_hat[r, c] x[c]
+ * fp32 products and sums (fmaf), summed per row in a fixed order, so repeated calls give
+ * identical results.  N == 0 writes y = 0.
+ * Errors: TCQ_EINVAL, TCQ_EUNSUPPORTED, TCQ_EHIP.
+ */
+int tcq_decode_gemv(const uint32_t *bitstream, const uint32_t *start_state,
+                    const float *codebook, int64_t M, int64_t N, int L, int k, int V, int T,
+                    const float *x, float *y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

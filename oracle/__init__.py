@@ -15,4 +15,6 @@ from .oracle import (  # noqa: F401
     path_cost,
     encode_matrix,
     nwords,
+    decode_matrix,
+    decode_gemv,
 )

@@ -186,3 +186,23 @@ def encode_matrix(W, d, C, L, k, V, T, blocks=None, threads=1):
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(one, range(nb)))
     return bits, s0, cost
+
+
+def decode_matrix(bits, s0, C, M, N, L, k, V, T):
+    """Reconstruction of an M x N matrix from per-block bitstreams (oracle decode of
+    every block, placed at W[r, c*T:(c+1)*T] for block r*(N/T)+c)."""
+    per_row = N // T
+    out = np.empty((M, N), dtype=np.float32)
+    bits = np.asarray(bits).view(np.uint32).reshape(M * per_row, -1)
+    s0 = np.asarray(s0).view(np.uint32).reshape(-1)
+    for b in range(M * per_row):
+        r, c = divmod(b, per_row)
+        out[r, c * T:(c + 1) * T] = decode_block(bits[b], int(s0[b]), C, L, k, V, T)
+    return out
+
+
+def decode_gemv(bits, s0, C, x, M, N, L, k, V, T):
+    """y = W_hat x for the decoded matrix W_hat, accumulated in float64 (the plain
+    definition: decode every block, then a matrix-vector product)."""
+    What = decode_matrix(bits, s0, C, M, N, L, k, V, T)
+    return What.astype(np.float64) @ np.asarray(x, dtype=np.float64), What

@@ -108,6 +108,27 @@ def test_decode_argument_checks():
     assert dec(M=0) == E.TCQ_OK
 
 
+def test_decode_gemv_argument_checks():
+    lib = _lib.load()
+    E = _lib
+
+    def gemv(**kw):
+        a = dict(bits=FAKE, s0=FAKE, cb=FAKE, M=2, N=512, L=16, k=2, V=1, T=256, x=FAKE,
+                 y=FAKE)
+        a.update(kw)
+        return lib.tcq_decode_gemv(a["bits"], a["s0"], a["cb"], a["M"], a["N"], a["L"],
+                                   a["k"], a["V"], a["T"], a["x"], a["y"], None)
+
+    assert gemv(N=500) == E.TCQ_EINVAL
+    assert gemv(x=None) == E.TCQ_EINVAL
+    assert gemv(y=None) == E.TCQ_EINVAL
+    assert gemv(k=16) == E.TCQ_EINVAL
+    assert gemv(L=20) == E.TCQ_EUNSUPPORTED
+    assert gemv(M=1 << 31) == E.TCQ_EUNSUPPORTED
+    assert "exceed" in tcq.tcq_last_error()
+    assert gemv(M=0) == E.TCQ_OK
+
+
 def test_workspace_sizes():
     mn = tcq.tcq_encode_workspace_min_bytes(16, 2, 1, 256)
     full = tcq.tcq_encode_workspace_bytes(2048, 2048, 16, 2, 1, 256)

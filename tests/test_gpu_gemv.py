@@ -1,0 +1,126 @@
+"""Fused decode + matrix-vector product (tcq_decode_gemv) vs. the oracle's decode
+followed by a float64 product.
+
+Inputs are seeded random bitstreams with start states below 2^(L-kV) (every such
+stream is a path of the trellis) and N(0,1) activations; nothing comes from the GPU
+encoder.  Bar: the GPU accumulates in fp32 with fmaf, each lane over at most
+ceil(N/64) products, then a tree of at most 8 additions, so for every row
+|y_gpu - y_ref| <= (N/64 + 16) * 2^-24 * sum_i |W_hat[r, i] x_i|  (recursive-summation
+bound, gamma_n <= n u, with margin).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+from trellis_coded_bit_amd import api  # noqa: E402
+
+
+def _say(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+def _random_streams(rng, nb, L, k, V, T):
+    nw = (k * T + 31) // 32
+    bits = rng.integers(0, 1 << 32, size=(nb, nw), dtype=np.uint64).astype(np.uint32)
+    tail = k * T % 32
+    if tail:
+        bits[:, -1] &= np.uint32(((1 << tail) - 1) << (32 - tail))
+    s0 = rng.integers(0, 1 << (L - k * V), size=nb, dtype=np.uint64).astype(np.uint32)
+    return bits, s0
+
+
+def _gpu_gemv(bits, s0, C, x, M, N, L, k, V, T):
+    bt = torch.from_numpy(bits.view(np.int32)).cuda()
+    st = torch.from_numpy(s0.view(np.int32)).cuda()
+    Ct = torch.from_numpy(np.ascontiguousarray(C)).cuda()
+    xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    y = api.decode_gemv(bt, st, Ct, xt, M, N, L, k, V, T)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _check(y, yref, What, x, N):
+    bound = (N / 64 + 16) * 2.0 ** -24 * (np.abs(What.astype(np.float64)) @
+                                          np.abs(x.astype(np.float64))) + 1e-30
+    err = np.abs(y.astype(np.float64) - yref)
+    bad = np.nonzero(err > bound)[0]
+    assert bad.size == 0, (f"{bad.size} rows off; first row {bad[0]}: gpu {y[bad[0]]!r} "
+                           f"ref {yref[bad[0]]!r} bound {bound[bad[0]]:.3e}")
+
+
+CASES = [
+    # L, k, V, T, M, N
+    (4, 1, 1, 12, 5, 36),
+    (6, 2, 1, 64, 9, 128),
+    (8, 2, 2, 32, 8, 96),
+    (9, 4, 1, 100, 6, 300),
+    (10, 3, 2, 30, 6, 120),
+    (12, 4, 2, 64, 3, 128),
+    (16, 2, 1, 256, 7, 2048 + 256),
+    (16, 3, 1, 256, 5, 1024),
+    (16, 2, 2, 256, 4, 768),
+    (16, 1, 1, 17, 3, 17 * 61),
+]
+
+
+@pytest.mark.parametrize("L,k,V,T,M,N", CASES)
+def test_gemv_parity_small(oracle_lib, L, k, V, T, M, N):
+    import oracle
+    _say(f"gemv L={L} k={k} V={V} T={T} M={M} N={N}")
+    rng = np.random.default_rng(L * 1000 + k * 100 + V * 10 + T)
+    C = oracle.make_codebook(L, V, 40 + L)
+    bits, s0 = _random_streams(rng, M * (N // T), L, k, V, T)
+    x = rng.standard_normal(N).astype(np.float32)
+    yref, What = oracle.decode_gemv(bits, s0, C, x, M, N, L, k, V, T)
+    y = _gpu_gemv(bits, s0, C, x, M, N, L, k, V, T)
+    _check(y, yref, What, x, N)
+    # unit vector: exactly the decoded column
+    e = np.zeros(N, np.float32)
+    e[N - 1] = 1.0
+    ye = _gpu_gemv(bits, s0, C, e, M, N, L, k, V, T)
+    assert np.array_equal(ye, What[:, N - 1])
+
+
+@pytest.mark.parametrize("M,N,L,k,V,T", [(2048, 2048, 16, 2, 1, 256),
+                                         (14336, 4096, 16, 2, 2, 256),
+                                         (4096, 14336, 16, 3, 1, 256)])
+def test_gemv_full_size_sampled_rows(oracle_lib, M, N, L, k, V, T):
+    """Full-size launch; the oracle checks 64 sampled rows (first, last, random)."""
+    import oracle
+    _say(f"gemv full M={M} N={N} L={L} k={k} V={V}")
+    rng = np.random.default_rng(M + N + k)
+    C = oracle.make_codebook(L, V, 3001)
+    per_row = N // T
+    bits, s0 = _random_streams(rng, M * per_row, L, k, V, T)
+    x = rng.standard_normal(N).astype(np.float32)
+    y = _gpu_gemv(bits, s0, C, x, M, N, L, k, V, T)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 62, replace=False)]))
+    sel = (rows[:, None] * per_row + np.arange(per_row)[None, :]).reshape(-1)
+    yref, What = oracle.decode_gemv(bits[sel], s0[sel], C, x, rows.size, N, L, k, V, T)
+    _check(y[rows], yref, What, x, N)
+
+
+def test_gemv_empty_and_deterministic(oracle_lib):
+    import oracle
+    L, k, V, T, M = 16, 2, 1, 256, 3
+    C = oracle.make_codebook(L, V, 1)
+    Ct = torch.from_numpy(C).cuda()
+    empty_i = torch.empty(0, dtype=torch.int32, device="cuda")
+    y = api.decode_gemv(empty_i, empty_i, Ct, torch.empty(0, device="cuda"), M, 0, L, k, V, T)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), np.zeros(M, np.float32))
+    rng = np.random.default_rng(9)
+    N = 4096
+    bits, s0 = _random_streams(rng, M * N // T, L, k, V, T)
+    x = rng.standard_normal(N).astype(np.float32)
+    y1 = _gpu_gemv(bits, s0, C, x, M, N, L, k, V, T)
+    y2 = _gpu_gemv(bits, s0, C, x, M, N, L, k, V, T)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))

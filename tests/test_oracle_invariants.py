@@ -162,3 +162,28 @@ def test_distortion_sanity_L16(oracle_lib):
     rate = k + (L - k * V) / T
     m = float(np.mean(mse))
     assert 2.0 ** (-2 * rate) < m < 0.1175, m
+
+
+def test_decode_gemv_definition(oracle_lib):
+    """The decode-then-matvec reference: a unit vector picks a decoded column, and the
+    product is linear in x."""
+    import oracle
+    L, k, V, T, M, N = 10, 2, 1, 32, 5, 96
+    rng = np.random.default_rng(21)
+    C = oracle.make_codebook(L, V, 4)
+    W = rng.standard_normal((M, N)).astype(np.float32)
+    bits, s0, _ = oracle.encode_matrix(W, None, C, L, k, V, T)
+    What = oracle.decode_matrix(bits, s0, C, M, N, L, k, V, T)
+    for j in (0, 31, 32, 95):
+        e = np.zeros(N, np.float32)
+        e[j] = 1.0
+        y, _ = oracle.decode_gemv(bits, s0, C, e, M, N, L, k, V, T)
+        assert np.array_equal(y, What[:, j].astype(np.float64))
+    x1 = rng.standard_normal(N).astype(np.float32)
+    x2 = rng.standard_normal(N).astype(np.float32)
+    y1, _ = oracle.decode_gemv(bits, s0, C, x1, M, N, L, k, V, T)
+    y2, _ = oracle.decode_gemv(bits, s0, C, x2, M, N, L, k, V, T)
+    y12, _ = oracle.decode_gemv(bits, s0, C, x1.astype(np.float64) + x2, M, N, L, k, V, T)
+    assert np.allclose(y12, y1 + y2, rtol=1e-12, atol=1e-12)
+    # every decoded weight is a codebook value of its block's path
+    assert set(np.unique(What)).issubset(set(C[:, 0].tolist()))

@@ -8,6 +8,7 @@ from . import _lib  # noqa: F401
 from ._lib import (  # noqa: F401
     TcqError,
     tcq_decode,
+    tcq_decode_gemv,
     tcq_encode,
     tcq_encode_timed,
     tcq_encode_workspace_bytes,

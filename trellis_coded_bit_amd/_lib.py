@@ -23,7 +23,7 @@ TCQ_ENOMEM = -5
 
 EXPORTED = ("tcq_version", "tcq_last_error", "tcq_make_codebook",
             "tcq_encode_workspace_bytes", "tcq_encode_workspace_min_bytes", "tcq_encode",
-            "tcq_encode_timed", "tcq_decode")
+            "tcq_encode_timed", "tcq_decode", "tcq_decode_gemv")
 
 _lib = None
 
@@ -62,6 +62,8 @@ def load():
                                      vp, i64, vp, sz, vp, vp, vp]
     lib.tcq_decode.restype = i32
     lib.tcq_decode.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, i64, vp]
+    lib.tcq_decode_gemv.restype = i32
+    lib.tcq_decode_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -126,3 +128,10 @@ def tcq_decode(bitstream: int, start_state: int, codebook: int, M: int, N: int, 
     _check("tcq_decode",
            load().tcq_decode(bitstream, start_state, codebook, M, N, L, k, V, T, out, ldo,
                              stream or None))
+
+
+def tcq_decode_gemv(bitstream: int, start_state: int, codebook: int, M: int, N: int, L: int,
+                    k: int, V: int, T: int, x: int, y: int, stream: int | None) -> None:
+    _check("tcq_decode_gemv",
+           load().tcq_decode_gemv(bitstream, start_state, codebook, M, N, L, k, V, T, x, y,
+                                  stream or None))

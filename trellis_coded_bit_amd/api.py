@@ -75,3 +75,12 @@ def decode(bitstream: torch.Tensor, start_state: torch.Tensor, codebook: torch.T
     _lib.tcq_decode(bitstream.data_ptr(), start_state.data_ptr(), codebook.data_ptr(), M, N,
                     L, k, V, T, out.data_ptr(), N, _stream())
     return out
+
+
+def decode_gemv(bitstream: torch.Tensor, start_state: torch.Tensor, codebook: torch.Tensor,
+                x: torch.Tensor, M: int, N: int, L: int, k: int, V: int, T: int) -> torch.Tensor:
+    assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous() and x.numel() == N
+    y = torch.empty(M, dtype=torch.float32, device=x.device)
+    _lib.tcq_decode_gemv(bitstream.data_ptr(), start_state.data_ptr(), codebook.data_ptr(), M,
+                         N, L, k, V, T, x.data_ptr(), y.data_ptr(), _stream())
+    return y

@@ -279,3 +279,26 @@ extern "C" int tcq_decode(const uint32_t *bitstream, const uint32_t *start_state
     if (e != hipSuccess) return hip_fail(fn, "decode launch", e);
     return TCQ_OK;
 }
+
+extern "C" int tcq_decode_gemv(const uint32_t *bitstream, const uint32_t *start_state,
+                               const float *codebook, int64_t M, int64_t N, int L, int k,
+                               int V, int T, const float *x, float *y, hipStream_t stream) {
+    clear_error();
+    const char *fn = "tcq_decode_gemv";
+    int rc = check_trellis(fn, M, N, L, k, V, T);
+    if (rc != TCQ_OK) return rc;
+    if (M == 0) return TCQ_OK;
+    if (!y || (N > 0 && (!bitstream || !start_state || !codebook || !x))) {
+        set_error("%s: bitstream, start_state, codebook, x and y must be non-NULL", fn);
+        return TCQ_EINVAL;
+    }
+    if (M > 0x7FFFFFFF || N / V > 0x7FFFFFFF) {
+        set_error("%s: M=%lld, N=%lld exceed one launch (at most 2^31-1 rows and 2^31-1 "
+                  "trellis steps per row)", fn, (long long)M, (long long)N);
+        return TCQ_EUNSUPPORTED;
+    }
+    hipError_t e = launch_decode_gemv(bitstream, start_state, codebook, x, y, M, N, L, k, V, T,
+                                      stream);
+    if (e != hipSuccess) return hip_fail(fn, "decode-GEMV launch", e);
+    return TCQ_OK;
+}

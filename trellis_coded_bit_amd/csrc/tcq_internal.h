@@ -50,6 +50,10 @@ hipError_t launch_decode(const uint32_t *bitstream, const uint32_t *start_state,
                          const float *C, int64_t M, int64_t N, int L, int k, int V, int T,
                          float *out, int64_t ldo, hipStream_t s);
 
+hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_state,
+                              const float *C, const float *x, float *y, int64_t M, int64_t N,
+                              int L, int k, int V, int T, hipStream_t s);
+
 // L = 16 register-resident path.
 bool l16_supported(const Problem &p);
 size_t l16_fixed_bytes(const Problem &p);
