@@ -17,4 +17,5 @@ from .oracle import (  # noqa: F401
     nwords,
     decode_matrix,
     decode_gemv,
+    ldlq_encode,
 )

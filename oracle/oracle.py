@@ -63,6 +63,10 @@ def _load():
     lib.oracle_path_cost.restype = ctypes.c_float
     lib.oracle_path_cost.argtypes = [_f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, _u32p, ctypes.c_uint32]
+    lib.oracle_ldlq_row.restype = ctypes.c_int
+    lib.oracle_ldlq_row.argtypes = [_f32p, _f32p, ctypes.c_long, _f32p, _f32p, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_long,
+                                    _u32p, _u32p, _f32p, _f32p, _f32p]
     _lib = lib
     return lib
 
@@ -206,3 +210,45 @@ def decode_gemv(bits, s0, C, x, M, N, L, k, V, T):
     definition: decode every block, then a matrix-vector product)."""
     What = decode_matrix(bits, s0, C, M, N, L, k, V, T)
     return What.astype(np.float64) @ np.asarray(x, dtype=np.float64), What
+
+
+def ldlq_encode(W, U, d, C, L, k, V, T, rows=None, threads=1):
+    """Error-feedback (LDLQ) encoding of the selected rows of W (default: all).
+
+    U is N x N float32, unit upper triangular with H = U diag(d) U^T; only entries
+    U[i, c] whose column block is later than the row's block are used.  Returns
+    (bits [rows, N/T, nwords], s0 [rows, N/T], cost [rows, N/T], W_hat [rows, N],
+    targets [rows, N]) as computed by tcq_oracle.c's oracle_ldlq_row.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    M, N = W.shape
+    assert N % T == 0
+    U = np.ascontiguousarray(U, dtype=np.float32)
+    assert U.shape == (N, N)
+    dd = _f32(d)
+    C = _f32(C)
+    rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    nblk = N // T
+    R = rows.size
+    bits = np.zeros((R, nblk, nwords(k, T)), dtype=np.uint32)
+    s0 = np.zeros((R, nblk), dtype=np.uint32)
+    cost = np.zeros((R, nblk), dtype=np.float32)
+    what = np.zeros((R, N), dtype=np.float32)
+    tgt = np.zeros((R, N), dtype=np.float32)
+    lib = _load()
+
+    def one(i):
+        w = np.ascontiguousarray(W[int(rows[i])])
+        rc = lib.oracle_ldlq_row(_fp(w), _fp(U), N, _fp(dd), _fp(C), L, k, V, T, N,
+                                 _up(bits[i]), _up(s0[i]), _fp(cost[i]), _fp(what[i]),
+                                 _fp(tgt[i]))
+        if rc != 0:
+            raise ValueError(f"oracle_ldlq_row failed ({rc})")
+
+    if threads <= 1:
+        for i in range(R):
+            one(i)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(R)))
+    return bits, s0, cost, what, tgt

@@ -29,6 +29,8 @@
  * With d == NULL the weight is exactly 1, and fmaf(e, e, acc) is used (fl(1*e) == e).
  * Ties: strict '<' over ascending predecessor index j, then the lowest end state.
  *
+ * Error feedback (LDLQ) over coding blocks: oracle_ldlq_row, with its own note below.
+ *
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fPIC -shared (no fast-math).
  */
 #include <math.h>
@@ -438,6 +440,53 @@ int oracle_two_best_block(const float *w, const float *d, const float *C, int L,
     free(J2);
     free(N1);
     free(N2);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Error feedback over coding blocks (LDLQ).                                  */
+/* Pingala-8 post, error-feedback toy and LDLQ paragraph: columns are          */
+/* quantized in order and each one's error is pushed onto the columns not yet  */
+/* quantized, with weights that come from H.  QTIP applies this per block of   */
+/* columns.  Reading: H = U diag(d) U^T with U unit upper triangular; column c */
+/* of block j (columns jT..jT+T-1) is coded against the target                 */
+/*     t_c = w_c + sum_{i < jT} (w_i - what_i) U[i][c],                        */
+/* evaluated in fp32 as acc = w_c; acc = fmaf(fl(w_i - what_i), U[i][c], acc)  */
+/* for i = 0, 1, ..., jT-1 in that order.  Then the proxy loss                 */
+/* (w - what) H (w - what)^T equals sum_c d_c eta_c^2 with eta = (w - what) U, */
+/* and eta_c = t_c - what_c when T = 1.  Entries of U inside a block are not   */
+/* used.  One row of W at a time (rows are independent).                       */
+/* ------------------------------------------------------------------------- */
+int oracle_ldlq_row(const float *w, const float *U, long ldu, const float *d, const float *C,
+                    int L, int k, int V, int T, long N, uint32_t *bits, uint32_t *s0_out,
+                    float *cost_out, float *what, float *target)
+{
+    if (!check_shape(L, k, V, T) || N < 0 || N % T != 0 || ldu < N)
+        return ORACLE_EINVAL;
+    const long nblk = N / T;
+    const long nw = ((long)k * T + 31) / 32;
+    float *err = (float *)malloc(sizeof(float) * (size_t)(N > 0 ? N : 1));
+    if (!err)
+        return ORACLE_ENOMEM;
+    for (long j = 0; j < nblk; ++j) {
+        const long c0 = j * T;
+        for (long c = c0; c < c0 + T; ++c) {
+            float acc = w[c];
+            for (long i = 0; i < c0; ++i)
+                acc = fmaf(err[i], U[i * ldu + c], acc);
+            target[c] = acc;
+        }
+        int rc = oracle_encode_block(target + c0, d ? d + c0 : NULL, C, L, k, V, T, -1,
+                                     bits + j * nw, s0_out + j, cost_out + j);
+        if (rc != ORACLE_OK) {
+            free(err);
+            return rc;
+        }
+        oracle_decode_block(bits + j * nw, s0_out[j], C, L, k, V, T, what + c0);
+        for (long i = c0; i < c0 + T; ++i)
+            err[i] = w[i] - what[i];
+    }
+    free(err);
     return ORACLE_OK;
 }
 

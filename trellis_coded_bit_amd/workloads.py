@@ -114,6 +114,54 @@ def ldl_diagonal(H: np.ndarray) -> np.ndarray:
     return np.diag(R) ** 2
 
 
+def udu_factor(H: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """H = U diag(d) U^T with U unit upper-triangular (float64), the factor that error
+    feedback in natural column order uses.  It is the LDL factorization of H in reversed
+    feature order: with P the reversal, P H P = R R^T (Cholesky), U = P R P diag(R)^-1
+    reversed, d = diag(R)^2 reversed."""
+    R = np.linalg.cholesky(H[::-1, ::-1])
+    r = np.diag(R).copy()
+    U = (R / r[None, :])[::-1, ::-1].copy()
+    return U, (r ** 2)[::-1].copy()
+
+
+def block_udu_factor(H: np.ndarray, T: int) -> tuple[np.ndarray, np.ndarray]:
+    """H = U D U^T with U unit upper block-triangular (identity T x T diagonal blocks)
+    and D block diagonal (float64): the factor error feedback over coding blocks of T
+    columns uses.  From the scalar factor H = U1 diag(d1) U1^T: the diagonal blocks
+    B_j of U1 give D_j = B_j diag(d1_j) B_j^T and U = U1 blockdiag(B)^-1.
+    Returns (U, D) with D as an array of the N/T diagonal blocks, shape (N/T, T, T).
+    T = 1 gives the scalar factor."""
+    N = H.shape[0]
+    assert N % T == 0
+    U1, d1 = udu_factor(H)
+    U = np.empty_like(U1)
+    D = np.empty((N // T, T, T))
+    for j in range(N // T):
+        s = slice(j * T, (j + 1) * T)
+        B = U1[s, s]
+        D[j] = (B * d1[s][None, :]) @ B.T
+        Binv = np.linalg.inv(B)
+        U[:j * T + T, s] = U1[:j * T + T, s] @ Binv
+        U[j * T + T:, s] = 0.0
+        U[s, s] = np.eye(T)
+    return U, D
+
+
+def make_ldlq_inputs(wl: Workload, N: int | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """(U, d) as float32 for error feedback over the workload's synthetic Hessian, with
+    U the block factor of block_udu_factor and d the diagonal of its D.  `N` restricts
+    to the first N features (for smaller tests)."""
+    X = make_samples(wl)
+    if N is not None:
+        X = X[:, :N]
+    H = hessian_from_samples(X)
+    del X
+    U, D = block_udu_factor(H, wl.T)
+    d = np.concatenate([np.diag(b) for b in D])
+    return U.astype(np.float32), d.astype(np.float32)
+
+
 def make_samples(wl: Workload) -> np.ndarray:
     """X: n_samples x N, rows AR(1) across the feature index with coefficient rho,
     then feature f scaled by exp(feat_sigma * u_f), u_f ~ N(0, 1)."""
