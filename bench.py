@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--cpu-threads", type=int, default=0, help="0: min(16, cpu count)")
     ap.add_argument("--gemv-iters", type=int, default=200,
                     help="calls of the fused decode+GEMV timed after the encoder (0: skip)")
+    ap.add_argument("--ldlq-workload", type=int, default=2,
+                    help="workload whose Hessian drives the timed error-feedback run (-1: skip)")
+    ap.add_argument("--ldlq-steps", type=int, default=1)
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES bytes (reference for "
@@ -128,6 +131,47 @@ def gemv_bench(torch, _lib, w, enc, Ct, iters):
     gbps = nbytes / (us / 1e6) / 1e9
     return {"us_per_call": us, "algorithmic_bytes": nbytes, "achieved_GBps": gbps,
             "frac_hbm": gbps / HBM_PEAK_GBPS, "weights_per_s": w.weights / (us / 1e6)}
+
+
+def ldlq_bench(torch, _lib, wl, index, steps):
+    """The error-feedback driver over a whole weighted workload: N/T encodes in sequence
+    with the feedback updates between them.  Inputs (W, the block factor U of the
+    workload's synthetic Hessian, d) are resident before timing."""
+    w = wl.WORKLOADS[index]
+    W = torch.from_numpy(wl.make_weights(w)).cuda()
+    U_np, d_np = wl.make_ldlq_inputs(w)
+    U = torch.from_numpy(U_np).cuda()
+    d = torch.from_numpy(d_np).cuda()
+    del U_np
+    C = torch.from_numpy(_lib.tcq_make_codebook(w.L, w.V, w.codebook_seed)).cuda()
+    from trellis_coded_bit_amd import api
+    ws = api.Workspace(_lib.tcq_ldlq_workspace_bytes(w.M, w.N, w.L, w.k, w.V, w.T), W.device)
+    nb = w.blocks
+    bits = torch.empty((nb, api.nwords(w.k, w.T)), dtype=torch.int32, device=W.device)
+    s0 = torch.empty(nb, dtype=torch.int32, device=W.device)
+    cost = torch.empty(nb, dtype=torch.float32, device=W.device)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        _lib.tcq_encode_ldlq(W.data_ptr(), w.M, w.N, w.N, U.data_ptr(), w.N, d.data_ptr(),
+                             C.data_ptr(), w.L, w.k, w.V, w.T, bits.data_ptr(), s0.data_ptr(),
+                             cost.data_ptr(), None, w.N, None, w.N, ws.ptr, ws.nbytes,
+                             stream.cuda_stream)
+
+    run()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    nblk = w.N // w.T
+    fma = w.M * w.T * sum(w.N - (j + 1) * w.T for j in range(nblk))
+    return {"workload": w.name, "ms": ms, "weights_per_s": w.weights / (ms / 1e3),
+            "column_blocks": nblk, "feedback_fma": fma}
 
 
 def main():
@@ -237,6 +281,9 @@ def main():
         log(f"[bench] fused decode+GEMV on the encoded matrix, {args.gemv_iters} calls",
             args.quiet)
         result["decode_gemv"] = gemv_bench(torch, _lib, w, out, Ct, args.gemv_iters)
+    if args.ldlq_workload >= 0:
+        log(f"[bench] error-feedback driver on workload {args.ldlq_workload}", args.quiet)
+        result["ldlq"] = ldlq_bench(torch, _lib, wl, args.ldlq_workload, args.ldlq_steps)
     if args.cpu_blocks > 0:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         log(f"[bench] cpu oracle on {args.cpu_blocks} blocks, {threads} threads", args.quiet)

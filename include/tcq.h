@@ -161,6 +161,43 @@ int tcq_decode_gemv(const uint32_t *bitstream, const uint32_t *start_state,
                     const float *codebook, int64_t M, int64_t N, int L, int k, int V, int T,
                     const float *x, float *y, hipStream_t stream);
 
+/*
+ * Error feedback over coding blocks (LDLQ).  Pingala-8 post, error-feedback toy and LDLQ
+ * paragraph: the columns are quantized in order and each one's error is pushed onto the
+ * columns not yet quantized, with weights from H (the average of x x^T over inputs);
+ * QTIP and CurveTQ code T columns at a time, so the feedback runs over coding blocks.
+ *
+ * With H = U D U^T, U unit upper block-triangular (identity T x T diagonal blocks) and D
+ * block diagonal, d = diag(D): block j (columns jT..jT+T-1) of every row is encoded
+ * exactly as tcq_encode would encode the target
+ *     t_c = w_c + sum_{i < jT} (w_i - what_i) U[i][c]
+ * with per-column weights d, where what is the reconstruction of the blocks already
+ * coded.  fp32 evaluation: acc = w_c; acc = fmaf(fl(w_i - what_i), U[i][c], acc) for
+ * i = 0..jT-1 ascending.  Only entries U[i][c] with i / T < c / T are read.
+ *
+ * tcq_ldlq_workspace_bytes -- device workspace for tcq_encode_ldlq with target and
+ *   recon both NULL (enough in every case).
+ * tcq_encode_ldlq
+ *   W           : device, M x N, leading dimension ldw >= N; not modified
+ *   U           : device, N x N, leading dimension ldu >= N (may be NULL when N == T)
+ *   d           : device, N floats, or NULL for d == 1
+ *   codebook, L, k, V, T, bitstream, start_state, cost : as tcq_encode (matrix layout:
+ *                 block r*(N/T)+j covers row r, columns jT..jT+T-1)
+ *   recon       : nullable device M x ldr; receives what
+ *   target      : nullable device M x ldt; receives the targets t (the library keeps them
+ *                 in the workspace when NULL)
+ *   workspace   : >= what tcq_ldlq_workspace_bytes reports
+ * Runs N/T encodes in sequence on `stream`; rows are independent.
+ * Errors: TCQ_EINVAL, TCQ_EUNSUPPORTED, TCQ_EWORKSPACE, TCQ_EHIP.
+ */
+int tcq_ldlq_workspace_bytes(int64_t M, int64_t N, int L, int k, int V, int T,
+                             size_t *bytes);
+int tcq_encode_ldlq(const float *W, int64_t M, int64_t N, int64_t ldw, const float *U,
+                    int64_t ldu, const float *d, const float *codebook, int L, int k, int V,
+                    int T, uint32_t *bitstream, uint32_t *start_state, float *cost,
+                    float *recon, int64_t ldr, float *target, int64_t ldt, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

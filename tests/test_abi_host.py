@@ -129,6 +129,35 @@ def test_decode_gemv_argument_checks():
     assert gemv(M=0) == E.TCQ_OK
 
 
+def test_encode_ldlq_argument_checks():
+    lib = _lib.load()
+    E = _lib
+
+    def run(**kw):
+        a = dict(W=FAKE, M=2, N=512, ldw=512, U=FAKE, ldu=512, d=None, cb=FAKE, L=16, k=2,
+                 V=1, T=256, bits=FAKE, s0=FAKE, cost=FAKE, recon=None, ldr=512, tgt=None,
+                 ldt=512, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.tcq_encode_ldlq(a["W"], a["M"], a["N"], a["ldw"], a["U"], a["ldu"], a["d"],
+                                   a["cb"], a["L"], a["k"], a["V"], a["T"], a["bits"],
+                                   a["s0"], a["cost"], a["recon"], a["ldr"], a["tgt"],
+                                   a["ldt"], a["ws"], a["wsb"], None)
+
+    assert run(N=500) == E.TCQ_EINVAL
+    assert run(U=None) == E.TCQ_EINVAL
+    assert run(ldu=100) == E.TCQ_EINVAL
+    assert run(ldw=100) == E.TCQ_EINVAL
+    assert run(recon=FAKE, ldr=10) == E.TCQ_EINVAL
+    assert run(tgt=FAKE, ldt=10) == E.TCQ_EINVAL
+    assert run(L=20) == E.TCQ_EUNSUPPORTED
+    assert run(wsb=100) == E.TCQ_EWORKSPACE
+    assert run(M=0) == E.TCQ_OK
+    assert tcq.tcq_ldlq_workspace_bytes(0, 512, 16, 2, 1, 256) == 0
+    big = tcq.tcq_ldlq_workspace_bytes(4, 512, 16, 2, 1, 256)
+    enc = tcq.tcq_encode_workspace_bytes(4, 256, 16, 2, 1, 256)
+    assert big >= enc + 4 * 512 * 4 + 4 * 256 * 4
+
+
 def test_workspace_sizes():
     mn = tcq.tcq_encode_workspace_min_bytes(16, 2, 1, 256)
     full = tcq.tcq_encode_workspace_bytes(2048, 2048, 16, 2, 1, 256)

@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     TcqError,
     tcq_decode,
     tcq_decode_gemv,
+    tcq_ldlq_workspace_bytes,
+    tcq_encode_ldlq,
     tcq_encode,
     tcq_encode_timed,
     tcq_encode_workspace_bytes,

@@ -23,7 +23,8 @@ TCQ_ENOMEM = -5
 
 EXPORTED = ("tcq_version", "tcq_last_error", "tcq_make_codebook",
             "tcq_encode_workspace_bytes", "tcq_encode_workspace_min_bytes", "tcq_encode",
-            "tcq_encode_timed", "tcq_decode", "tcq_decode_gemv")
+            "tcq_encode_timed", "tcq_decode", "tcq_decode_gemv",
+            "tcq_ldlq_workspace_bytes", "tcq_encode_ldlq")
 
 _lib = None
 
@@ -64,6 +65,12 @@ def load():
     lib.tcq_decode.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, i64, vp]
     lib.tcq_decode_gemv.restype = i32
     lib.tcq_decode_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, vp, vp]
+    lib.tcq_ldlq_workspace_bytes.restype = i32
+    lib.tcq_ldlq_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32,
+                                             ctypes.POINTER(ctypes.c_size_t)]
+    lib.tcq_encode_ldlq.restype = i32
+    lib.tcq_encode_ldlq.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, i32, i32, i32, i32,
+                                    vp, vp, vp, vp, i64, vp, i64, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -134,4 +141,23 @@ def tcq_decode_gemv(bitstream: int, start_state: int, codebook: int, M: int, N: 
                     k: int, V: int, T: int, x: int, y: int, stream: int | None) -> None:
     _check("tcq_decode_gemv",
            load().tcq_decode_gemv(bitstream, start_state, codebook, M, N, L, k, V, T, x, y,
+                                  stream or None))
+
+
+def tcq_ldlq_workspace_bytes(M: int, N: int, L: int, k: int, V: int, T: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check("tcq_ldlq_workspace_bytes",
+           load().tcq_ldlq_workspace_bytes(M, N, L, k, V, T, ctypes.byref(b)))
+    return int(b.value)
+
+
+def tcq_encode_ldlq(W: int, M: int, N: int, ldw: int, U: int | None, ldu: int,
+                    d: int | None, codebook: int, L: int, k: int, V: int, T: int,
+                    bitstream: int, start_state: int, cost: int, recon: int | None, ldr: int,
+                    target: int | None, ldt: int, workspace: int, workspace_bytes: int,
+                    stream: int | None) -> None:
+    _check("tcq_encode_ldlq",
+           load().tcq_encode_ldlq(W, M, N, ldw, U or None, ldu, d or None, codebook, L, k, V,
+                                  T, bitstream, start_state, cost, recon or None, ldr,
+                                  target or None, ldt, workspace, workspace_bytes,
                                   stream or None))

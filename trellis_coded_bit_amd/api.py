@@ -84,3 +84,37 @@ def decode_gemv(bitstream: torch.Tensor, start_state: torch.Tensor, codebook: to
     _lib.tcq_decode_gemv(bitstream.data_ptr(), start_state.data_ptr(), codebook.data_ptr(), M,
                          N, L, k, V, T, x.data_ptr(), y.data_ptr(), _stream())
     return y
+
+
+@dataclass
+class EncodedLdlq(Encoded):
+    target: torch.Tensor | None = None  # float32 [M, N]
+
+
+def encode_ldlq(W: torch.Tensor, U: torch.Tensor | None, d: torch.Tensor | None,
+                codebook: torch.Tensor, L: int, k: int, V: int, T: int, recon: bool = True,
+                target: bool = False, workspace: Workspace | None = None) -> EncodedLdlq:
+    assert W.is_cuda and W.dtype == torch.float32 and W.dim() == 2 and W.stride(1) == 1
+    M, N = W.shape
+    if U is not None:
+        assert U.is_cuda and U.dtype == torch.float32 and U.dim() == 2 and U.stride(1) == 1
+    if d is not None:
+        assert d.is_cuda and d.dtype == torch.float32 and d.is_contiguous() and d.numel() == N
+    nb = M * (N // T)
+    dev = W.device
+    out = EncodedLdlq(
+        bitstream=torch.empty((nb, nwords(k, T)), dtype=torch.int32, device=dev),
+        start_state=torch.empty(nb, dtype=torch.int32, device=dev),
+        cost=torch.empty(nb, dtype=torch.float32, device=dev),
+        recon=torch.empty((M, N), dtype=torch.float32, device=dev) if recon else None,
+        target=torch.empty((M, N), dtype=torch.float32, device=dev) if target else None)
+    if workspace is None:
+        workspace = Workspace(_lib.tcq_ldlq_workspace_bytes(M, N, L, k, V, T), dev)
+    _lib.tcq_encode_ldlq(W.data_ptr(), M, N, W.stride(0),
+                         None if U is None else U.data_ptr(), N if U is None else U.stride(0),
+                         None if d is None else d.data_ptr(), codebook.data_ptr(), L, k, V, T,
+                         out.bitstream.data_ptr(), out.start_state.data_ptr(),
+                         out.cost.data_ptr(), None if out.recon is None else out.recon.data_ptr(),
+                         N, None if out.target is None else out.target.data_ptr(), N,
+                         workspace.ptr, workspace.nbytes, _stream())
+    return out

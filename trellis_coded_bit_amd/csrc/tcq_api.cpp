@@ -302,3 +302,122 @@ extern "C" int tcq_decode_gemv(const uint32_t *bitstream, const uint32_t *start_
     if (e != hipSuccess) return hip_fail(fn, "decode-GEMV launch", e);
     return TCQ_OK;
 }
+
+// Error feedback (LDLQ) driver: workspace layout
+//   [targets M x N, unless the caller passes `target`]
+//   [reconstruction slice M x T, unless the caller passes `recon`]
+//   [slice bitstreams M x nwords][slice start states M][slice costs M]
+//   [encoder workspace for an M x T problem: the rest]
+namespace {
+struct LdlqLayout {
+    size_t tgt, rh, sbits, sstart, scost, enc;  // byte offsets
+    size_t fixed;                               // bytes before the encoder workspace
+};
+
+LdlqLayout ldlq_layout(int64_t M, int64_t N, int k, int T, bool own_tgt, bool own_rh) {
+    LdlqLayout l{};
+    const size_t nw = (static_cast<size_t>(k) * T + 31) / 32;
+    size_t off = 0;
+    l.tgt = off;
+    if (own_tgt) off += align_up(static_cast<size_t>(M) * N * sizeof(float), 256);
+    l.rh = off;
+    if (own_rh) off += align_up(static_cast<size_t>(M) * T * sizeof(float), 256);
+    l.sbits = off;
+    off += align_up(static_cast<size_t>(M) * nw * sizeof(uint32_t), 256);
+    l.sstart = off;
+    off += align_up(static_cast<size_t>(M) * sizeof(uint32_t), 256);
+    l.scost = off;
+    off += align_up(static_cast<size_t>(M) * sizeof(float), 256);
+    l.enc = off;
+    l.fixed = off;
+    return l;
+}
+}  // namespace
+
+extern "C" int tcq_ldlq_workspace_bytes(int64_t M, int64_t N, int L, int k, int V, int T,
+                                        size_t *bytes) {
+    clear_error();
+    const char *fn = "tcq_ldlq_workspace_bytes";
+    int rc = check_trellis(fn, M, N, L, k, V, T);
+    if (rc != TCQ_OK) return rc;
+    if (!bytes) {
+        set_error("%s: bytes is NULL", fn);
+        return TCQ_EINVAL;
+    }
+    if (M == 0 || N == 0) {
+        *bytes = 0;
+        return TCQ_OK;
+    }
+    size_t enc = 0;
+    rc = tcq_encode_workspace_bytes(M, T, L, k, V, T, &enc);
+    if (rc != TCQ_OK) return rc;
+    *bytes = ldlq_layout(M, N, k, T, true, true).fixed + enc;
+    return TCQ_OK;
+}
+
+extern "C" int tcq_encode_ldlq(const float *W, int64_t M, int64_t N, int64_t ldw,
+                               const float *U, int64_t ldu, const float *d,
+                               const float *codebook, int L, int k, int V, int T,
+                               uint32_t *bitstream, uint32_t *start_state, float *cost,
+                               float *recon, int64_t ldr, float *target, int64_t ldt,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    clear_error();
+    const char *fn = "tcq_encode_ldlq";
+    int rc = check_trellis(fn, M, N, L, k, V, T);
+    if (rc != TCQ_OK) return rc;
+    if (M == 0 || N == 0) return TCQ_OK;
+    const int64_t nbpr = N / T;
+    if (!W || !codebook || !bitstream || !start_state || !cost || (nbpr > 1 && !U)) {
+        set_error("%s: W, codebook, bitstream, start_state, cost and (for N > T) U must be "
+                  "non-NULL", fn);
+        return TCQ_EINVAL;
+    }
+    if (ldw < N || (nbpr > 1 && ldu < N) || (recon && ldr < N) || (target && ldt < N)) {
+        set_error("%s: leading dimensions must be >= N=%lld (ldw=%lld ldu=%lld ldr=%lld "
+                  "ldt=%lld)", fn, (long long)N, (long long)ldw, (long long)ldu,
+                  (long long)ldr, (long long)ldt);
+        return TCQ_EINVAL;
+    }
+    const LdlqLayout lay = ldlq_layout(M, N, k, T, target == nullptr, recon == nullptr);
+    size_t enc_min = 0;
+    rc = tcq_encode_workspace_min_bytes(L, k, V, T, &enc_min);
+    if (rc != TCQ_OK) return rc;
+    clear_error();
+    if (!workspace || workspace_bytes < lay.fixed + enc_min) {
+        set_error("%s: workspace of %zu bytes is below the minimum %zu", fn,
+                  workspace ? workspace_bytes : size_t{0}, lay.fixed + enc_min);
+        return TCQ_EWORKSPACE;
+    }
+    char *ws = static_cast<char *>(workspace);
+    float *tgt = target ? target : reinterpret_cast<float *>(ws + lay.tgt);
+    const int64_t lt = target ? ldt : N;
+    uint32_t *sbits = reinterpret_cast<uint32_t *>(ws + lay.sbits);
+    uint32_t *sstart = reinterpret_cast<uint32_t *>(ws + lay.sstart);
+    float *scost = reinterpret_cast<float *>(ws + lay.scost);
+    const int nw = (k * T + 31) / 32;
+
+    hipError_t e = hipMemcpy2DAsync(tgt, static_cast<size_t>(lt) * sizeof(float), W,
+                                    static_cast<size_t>(ldw) * sizeof(float),
+                                    static_cast<size_t>(N) * sizeof(float),
+                                    static_cast<size_t>(M), hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return hip_fail(fn, "target copy", e);
+    for (int64_t j = 0; j < nbpr; ++j) {
+        const int64_t c0 = j * T;
+        float *rh = recon ? recon + c0 : reinterpret_cast<float *>(ws + lay.rh);
+        const int64_t ldh = recon ? ldr : T;
+        rc = encode_impl(fn, tgt + c0, M, T, lt, d ? d + c0 : nullptr, codebook, L, k, V, T,
+                         sbits, sstart, scost, rh, ldh, ws + lay.enc,
+                         workspace_bytes - lay.enc, stream, nullptr, nullptr);
+        if (rc != TCQ_OK) return rc;
+        e = launch_ldlq_scatter(sbits, sstart, scost, M, nw, nbpr, j, bitstream, start_state,
+                                cost, stream);
+        if (e != hipSuccess) return hip_fail(fn, "slice scatter launch", e);
+        if (j + 1 < nbpr) {
+            e = launch_ldlq_update(tgt, lt, W, ldw, rh, ldh, U, ldu, M, c0 + T, N, c0, T,
+                                   stream);
+            if (e != hipSuccess) return hip_fail(fn, "feedback update launch", e);
+        }
+    }
+    return TCQ_OK;
+}

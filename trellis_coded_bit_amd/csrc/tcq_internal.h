@@ -54,6 +54,16 @@ hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_s
                               const float *C, const float *x, float *y, int64_t M, int64_t N,
                               int L, int k, int V, int T, hipStream_t s);
 
+// Error feedback over coding blocks.
+hipError_t launch_ldlq_update(float *tgt, int64_t ldt, const float *W, int64_t ldw,
+                              const float *what, int64_t ldh, const float *U, int64_t ldu,
+                              int64_t M, int64_t c_begin, int64_t c_end, int64_t i0, int T,
+                              hipStream_t s);
+hipError_t launch_ldlq_scatter(const uint32_t *sbits, const uint32_t *sstart,
+                               const float *scost, int64_t M, int nwords, int64_t nbpr,
+                               int64_t j, uint32_t *bitstream, uint32_t *start_state,
+                               float *cost, hipStream_t s);
+
 // L = 16 register-resident path.
 bool l16_supported(const Problem &p);
 size_t l16_fixed_bytes(const Problem &p);
