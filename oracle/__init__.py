@@ -18,4 +18,6 @@ from .oracle import (  # noqa: F401
     decode_matrix,
     decode_gemv,
     ldlq_encode,
+    bcjr_block,
+    bcjr_matrix,
 )

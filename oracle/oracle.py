@@ -67,6 +67,11 @@ def _load():
     lib.oracle_ldlq_row.argtypes = [_f32p, _f32p, ctypes.c_long, _f32p, _f32p, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_long,
                                     _u32p, _u32p, _f32p, _f32p, _f32p]
+    _f64p = ctypes.POINTER(ctypes.c_double)
+    lib.oracle_bcjr_block.restype = ctypes.c_int
+    lib.oracle_bcjr_block.argtypes = [_f64p, _f64p, _f32p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_double, _f64p,
+                                      _f64p]
     _lib = lib
     return lib
 
@@ -252,3 +257,48 @@ def ldlq_encode(W, U, d, C, L, k, V, T, rows=None, threads=1):
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(one, range(R)))
     return bits, s0, cost, what, tgt
+
+
+def bcjr_block(w, d, C, L, k, V, T, tau):
+    """Soft codeword (float64 [T]) and log Z (natural log) of one block at temperature
+    tau; w and d are taken in float64 (pass float32 data to match the GPU's inputs)."""
+    f64p = ctypes.POINTER(ctypes.c_double)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    dd = None if d is None else np.ascontiguousarray(d, dtype=np.float64)
+    C = _f32(C)
+    assert w.size == T and C.size == (1 << L) * V
+    soft = np.empty(T, dtype=np.float64)
+    logz = ctypes.c_double(0)
+    rc = _load().oracle_bcjr_block(w.ctypes.data_as(f64p),
+                                   None if dd is None else dd.ctypes.data_as(f64p), _fp(C),
+                                   L, k, V, T, float(tau), soft.ctypes.data_as(f64p),
+                                   ctypes.byref(logz))
+    if rc != 0:
+        raise ValueError(f"oracle_bcjr_block failed ({rc})")
+    return soft, float(logz.value)
+
+
+def bcjr_matrix(W, d, C, L, k, V, T, tau, blocks=None, threads=1):
+    """Soft codewords [nb, T] and log Z [nb] for the selected blocks of W (block
+    b = r*(N/T)+c covers W[r, cT:(c+1)T] and d[cT:(c+1)T])."""
+    W = np.asarray(W, dtype=np.float32)
+    M, N = W.shape
+    per_row = N // T
+    blocks = np.arange(M * per_row) if blocks is None else np.asarray(blocks, dtype=np.int64)
+    soft = np.zeros((blocks.size, T), dtype=np.float64)
+    logz = np.zeros(blocks.size, dtype=np.float64)
+    dd = None if d is None else np.asarray(d, dtype=np.float32)
+
+    def one(i):
+        r, c = divmod(int(blocks[i]), per_row)
+        soft[i], logz[i] = bcjr_block(W[r, c * T:(c + 1) * T],
+                                      None if dd is None else dd[c * T:(c + 1) * T], C, L,
+                                      k, V, T, tau)
+
+    if threads <= 1:
+        for i in range(blocks.size):
+            one(i)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(blocks.size)))
+    return soft, logz

@@ -30,6 +30,7 @@
  * Ties: strict '<' over ascending predecessor index j, then the lowest end state.
  *
  * Error feedback (LDLQ) over coding blocks: oracle_ldlq_row, with its own note below.
+ * Soft trellis (BCJR) at a temperature: oracle_bcjr_block, with its own note below.
  *
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fPIC -shared (no fast-math).
  */
@@ -487,6 +488,118 @@ int oracle_ldlq_row(const float *w, const float *U, long ldu, const float *d, co
             err[i] = w[i] - what[i];
     }
     free(err);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Soft trellis (BCJR) at temperature tau.                                     */
+/* BCJR-QAT abstract on the aqora listing: replace the Viterbi argmax by the   */
+/* BCJR forward-backward sum-product at a temperature, giving a soft codeword  */
+/* equal to the Boltzmann expectation over trellis paths, which tends to the   */
+/* hard code as the temperature goes to 0.  Reading: every path of the block   */
+/* (free start: s_1 may be any of the 2^L states) has energy J, the same       */
+/* weighted squared error the Viterbi search minimises, and probability        */
+/* exp(-J / tau) / Z.  The soft codeword of weight (t-1)V+v is the expectation */
+/* of C[s_t][v].  Computed in double with natural logarithms:                  */
+/*   g_t(s)     = -sum_v d (w - C[s][v])^2 / tau                               */
+/*   a_1(s)     = g_1(s);  a_t(s') = g_t(s') + LSE over predecessors s of      */
+/*                a_{t-1}(s)                                                   */
+/*   b_n(s)     = 0;       b_t(s)  = LSE over successors s' of                 */
+/*                (g_{t+1}(s') + b_{t+1}(s'))                                  */
+/*   log Z      = LSE_s a_n(s);  P(s_t = s) = exp(a_t(s) + b_t(s) - log Z)     */
+/* LSE(v) = max(v) + log(sum exp(v - max(v))).                                 */
+/* ------------------------------------------------------------------------- */
+static double lse_update(double m, double *sum, double v)
+{
+    /* running log-sum-exp: (m, sum) represents m + log(sum) */
+    if (v <= m) {
+        *sum += exp(v - m);
+        return m;
+    }
+    *sum = *sum * exp(m - v) + 1.0;
+    return v;
+}
+
+int oracle_bcjr_block(const double *w, const double *d, const float *C, int L, int k, int V,
+                      int T, double tau, double *soft_out, double *logz_out)
+{
+    if (!check_shape(L, k, V, T) || !(tau > 0.0))
+        return ORACLE_EINVAL;
+    const int n = T / V;
+    const int kv = k * V;
+    const long S = 1L << L;
+    const long mask = S - 1;
+    const int G = 1 << kv;
+    double *g = (double *)malloc(sizeof(double) * (size_t)S * (size_t)n);
+    double *a = (double *)malloc(sizeof(double) * (size_t)S * (size_t)n);
+    double *b = (double *)malloc(sizeof(double) * (size_t)S);
+    double *bn = (double *)malloc(sizeof(double) * (size_t)S);
+    if (!g || !a || !b || !bn) {
+        free(g);
+        free(a);
+        free(b);
+        free(bn);
+        return ORACLE_ENOMEM;
+    }
+    for (int t = 0; t < n; ++t) {
+        for (long s = 0; s < S; ++s) {
+            double m = 0.0;
+            for (int v = 0; v < V; ++v) {
+                const int i = t * V + v;
+                const double e = w[i] - (double)C[s * V + v];
+                m += (d ? d[i] : 1.0) * e * e;
+            }
+            g[(long)t * S + s] = -m / tau;
+        }
+    }
+    /* forward */
+    for (long s = 0; s < S; ++s)
+        a[s] = g[s];
+    for (int t = 1; t < n; ++t) {
+        for (long s2 = 0; s2 < S; ++s2) {
+            const long x = s2 >> kv; /* predecessors: (j << (L - kv)) | x */
+            double m = -INFINITY, sum = 0.0;
+            for (int j = 0; j < G; ++j) {
+                const long s1 = ((long)j << (L - kv)) | x;
+                m = lse_update(m, &sum, a[(long)(t - 1) * S + s1]);
+            }
+            a[(long)t * S + s2] = g[(long)t * S + s2] + m + log(sum);
+        }
+    }
+    double m = -INFINITY, sum = 0.0;
+    for (long s = 0; s < S; ++s)
+        m = lse_update(m, &sum, a[(long)(n - 1) * S + s]);
+    const double logz = m + log(sum);
+    *logz_out = logz;
+    /* backward, with the expectation at each step */
+    for (long s = 0; s < S; ++s)
+        b[s] = 0.0;
+    for (int t = n - 1; t >= 0; --t) {
+        for (int v = 0; v < V; ++v) {
+            double acc = 0.0;
+            for (long s = 0; s < S; ++s) {
+                const double p = exp(a[(long)t * S + s] + b[s] - logz);
+                acc += p * (double)C[s * V + v];
+            }
+            soft_out[t * V + v] = acc;
+        }
+        if (t == 0)
+            break;
+        for (long s = 0; s < S; ++s) {
+            double mm = -INFINITY, ss = 0.0;
+            for (int bb = 0; bb < G; ++bb) {
+                const long s2 = ((s << kv) | bb) & mask;
+                mm = lse_update(mm, &ss, g[(long)t * S + s2] + b[s2]);
+            }
+            bn[s] = mm + log(ss);
+        }
+        for (long s = 0; s < S; ++s)
+            b[s] = bn[s];
+    }
+    free(g);
+    free(a);
+    free(b);
+    free(bn);
     return ORACLE_OK;
 }
 
