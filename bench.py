@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--cpu-threads", type=int, default=0, help="0: min(16, cpu count)")
     ap.add_argument("--gemv-iters", type=int, default=200,
                     help="calls of the fused decode+GEMV timed after the encoder (0: skip)")
+    ap.add_argument("--bcjr-tau", type=float, default=0.1,
+                    help="temperature of the timed soft-trellis run (0: skip)")
     ap.add_argument("--ldlq-workload", type=int, default=2,
                     help="workload whose Hessian drives the timed error-feedback run (-1: skip)")
     ap.add_argument("--ldlq-steps", type=int, default=1)
@@ -174,6 +176,33 @@ def ldlq_bench(torch, _lib, wl, index, steps):
             "column_blocks": nblk, "feedback_fma": fma}
 
 
+def bcjr_bench(torch, _lib, w, Wt, dt_, Ct, tau, steps):
+    """Soft trellis (forward-backward at temperature tau) over the whole bench workload."""
+    from trellis_coded_bit_amd import api
+    ws = api.Workspace(_lib.tcq_bcjr_workspace_bytes(w.M, w.N, w.L, w.k, w.V, w.T), Wt.device)
+    soft = torch.empty((w.M, w.N), dtype=torch.float32, device=Wt.device)
+    logz = torch.empty(w.blocks, dtype=torch.float32, device=Wt.device)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        _lib.tcq_bcjr(Wt.data_ptr(), w.M, w.N, w.N, None if dt_ is None else dt_.data_ptr(),
+                      Ct.data_ptr(), w.L, w.k, w.V, w.T, tau, soft.data_ptr(), w.N,
+                      logz.data_ptr(), ws.ptr, ws.nbytes, stream.cuda_stream)
+
+    run()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    updates = w.blocks * (w.T // w.V) * (1 << w.L)
+    return {"tau": tau, "ms": ms, "weights_per_s": w.weights / (ms / 1e3),
+            "state_updates_per_s_per_pass": updates / (ms / 1e3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -281,6 +310,9 @@ def main():
         log(f"[bench] fused decode+GEMV on the encoded matrix, {args.gemv_iters} calls",
             args.quiet)
         result["decode_gemv"] = gemv_bench(torch, _lib, w, out, Ct, args.gemv_iters)
+    if args.bcjr_tau > 0:
+        log(f"[bench] soft trellis at tau={args.bcjr_tau}", args.quiet)
+        result["bcjr"] = bcjr_bench(torch, _lib, w, Wt, dt_, Ct, args.bcjr_tau, 1)
     if args.ldlq_workload >= 0:
         log(f"[bench] error-feedback driver on workload {args.ldlq_workload}", args.quiet)
         result["ldlq"] = ldlq_bench(torch, _lib, wl, args.ldlq_workload, args.ldlq_steps)

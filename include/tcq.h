@@ -198,6 +198,37 @@ int tcq_encode_ldlq(const float *W, int64_t M, int64_t N, int64_t ldw, const flo
                     float *recon, int64_t ldr, float *target, int64_t ldt, void *workspace,
                     size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Soft trellis (BCJR) at temperature tau.  BCJR-QAT abstract on the aqora listing: the
+ * Viterbi argmax is replaced by the BCJR forward-backward sum-product at a temperature;
+ * the soft codeword is the Boltzmann expectation of the emitted values over all paths,
+ * and the hard (Viterbi) code comes back as the temperature goes to 0.
+ *
+ * Every path of a block (free start, as tcq_encode) has energy J, the same weighted
+ * squared error tcq_encode minimises, and probability exp(-J / tau) / Z.
+ *   soft[r][cT + i] = E[ what_i ] over that distribution (block r*(N/T)+c)
+ *   logz[b]         = log Z of block b (natural log), nullable
+ * fp32 branch metrics (the encoder's chain), base-2 log-sum-exp in fp32 with the hardware
+ * exp2/log2, per-step shifts summed in double for log Z.  Results are deterministic.
+ * Supported: every tcq_encode shape with k*V <= 4.
+ *
+ * tcq_bcjr_workspace_bytes -- recommended workspace (a batch of blocks); the minimum is
+ *   one block: (T/V) * 2^(L-kV) * 4 bytes rounded up to 256, plus 2 * 2^(L-kV) * 4 when
+ *   2 * 2^(L-kV) * 4 > 128 KiB.
+ * tcq_bcjr
+ *   W, M, N, ldw, d, codebook, L, k, V, T : as tcq_encode (device pointers)
+ *   tau    : temperature, > 0 and finite
+ *   soft   : device out, M x ldo (ldo >= N)
+ *   logz   : nullable device out, M*N/T floats
+ * Errors: TCQ_EINVAL, TCQ_EUNSUPPORTED (k*V > 4), TCQ_EWORKSPACE, TCQ_EHIP.
+ */
+int tcq_bcjr_workspace_bytes(int64_t M, int64_t N, int L, int k, int V, int T,
+                             size_t *bytes);
+int tcq_bcjr(const float *W, int64_t M, int64_t N, int64_t ldw, const float *d,
+             const float *codebook, int L, int k, int V, int T, float tau, float *soft,
+             int64_t ldo, float *logz, void *workspace, size_t workspace_bytes,
+             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

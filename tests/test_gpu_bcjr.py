@@ -1,0 +1,129 @@
+"""Soft trellis (tcq_bcjr) on the GPU vs. oracle.bcjr_block (float64).
+
+Tolerance, from the arithmetic: the GPU carries base-2 log-weights in fp32.  A
+log-weight that matters (its path has non-negligible probability) has magnitude about
+32 + log2(e) * J*/(n tau) per step (J* = the block's Viterbi cost), and each of the 2n
+forward/backward steps adds a few roundings of that size; taken as a random walk this
+is u * sqrt(2n) * (32 + 1.4427 J*/(n tau)) in log2 units, which moves a probability by
+ln 2 times that, and the soft codeword by at most that times max|C|.  The test allows
+twice this.  log Z (natural log) is a sum of n shifted terms plus one fp32 rounding:
+|error| <= 8 u (n + |log Z|).  u = 2^-24.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from trellis_coded_bit_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+from trellis_coded_bit_amd import api  # noqa: E402
+
+U32 = 2.0 ** -24
+
+
+def _say(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+def _gpu(W, d, C, L, k, V, T, tau):
+    soft, logz = api.bcjr(torch.from_numpy(np.ascontiguousarray(W)).cuda(),
+                          None if d is None else torch.from_numpy(d).cuda(),
+                          torch.from_numpy(C).cuda(), L, k, V, T, tau)
+    torch.cuda.synchronize()
+    return soft.cpu().numpy(), logz.cpu().numpy()
+
+
+def _check(soft, logz, W, d, C, L, k, V, T, tau, blocks, threads=8):
+    import oracle
+    M, N = W.shape
+    per_row = N // T
+    n = T // V
+    rs, rz = oracle.bcjr_matrix(W, d, C, L, k, V, T, tau, blocks=blocks, threads=threads)
+    _, _, jstar = oracle.encode_matrix(W, d, C, L, k, V, T, blocks=blocks, threads=threads)
+    cmax = float(np.abs(C).max())
+    worst = 0.0
+    for i, b in enumerate(blocks):
+        r, c = divmod(int(b), per_row)
+        g = soft[r, c * T:(c + 1) * T].astype(np.float64)
+        scale = 32.0 + 1.4426950408889634 * float(jstar[i]) / (n * tau)
+        tol = 2.0 * U32 * np.sqrt(2 * n) * scale * np.log(2.0) * cmax
+        err = float(np.abs(g - rs[i]).max())
+        worst = max(worst, err / tol)
+        assert err <= tol, f"block {b}: soft error {err:.3e} > {tol:.3e}"
+        ztol = 8 * U32 * (n + abs(rz[i]))
+        assert abs(float(logz[b]) - rz[i]) <= ztol, (b, float(logz[b]), rz[i], ztol)
+    return worst
+
+
+CASES = [
+    # L, k, V, T, M, N, weighted
+    (4, 1, 1, 8, 3, 24, False),
+    (6, 2, 1, 16, 3, 48, True),
+    (8, 2, 1, 64, 2, 128, True),
+    (8, 2, 2, 32, 2, 64, True),
+    (10, 3, 1, 30, 2, 60, False),
+    (12, 4, 1, 64, 2, 128, True),
+    (11, 2, 1, 256, 1, 256, True),
+    (16, 2, 1, 256, 1, 512, True),
+    (16, 3, 1, 256, 1, 256, True),
+    (16, 2, 2, 256, 1, 256, False),
+    (16, 1, 1, 40, 1, 80, True),
+]
+
+
+@pytest.mark.parametrize("L,k,V,T,M,N,weighted", CASES)
+@pytest.mark.parametrize("tau", [0.01, 0.1, 1.0])
+def test_bcjr_parity(oracle_lib, L, k, V, T, M, N, weighted, tau):
+    import oracle
+    _say(f"bcjr L={L} k={k} V={V} T={T} M={M} N={N} weighted={weighted} tau={tau}")
+    rng = np.random.default_rng(L * 7 + T + M)
+    C = oracle.make_codebook(L, V, 90 + L)
+    W = rng.standard_normal((M, N)).astype(np.float32)
+    d = np.exp(0.5 * rng.standard_normal(N)).astype(np.float32) if weighted else None
+    soft, logz = _gpu(W, d, C, L, k, V, T, tau)
+    worst = _check(soft, logz, W, d, C, L, k, V, T, tau, np.arange(M * (N // T)))
+    _say(f"  worst error / tolerance {worst:.3f}")
+
+
+def test_bcjr_low_temperature_is_viterbi(oracle_lib):
+    """tau far below the runner-up gap: the soft codeword is the Viterbi reconstruction."""
+    import oracle
+    L, k, V, T = 16, 2, 1, 256
+    C = oracle.make_codebook(L, V, 5)
+    rng = np.random.default_rng(2)
+    W = rng.standard_normal((4, T)).astype(np.float32)
+    gaps = []
+    for r in range(4):
+        best, second = oracle.two_best_block(W[r], None, C, L, k, V, T)
+        gaps.append(float(second) - float(best))
+    r = int(np.argmax(gaps))
+    tau = gaps[r] / 60.0
+    bits, s0, _ = oracle.encode_block(W[r], None, C, L, k, V, T)
+    hard = oracle.decode_block(bits, s0, C, L, k, V, T)
+    soft, _ = _gpu(W[r:r + 1], None, C, L, k, V, T, tau)
+    assert np.allclose(soft[0], hard, atol=1e-4)
+
+
+def test_bcjr_full_size_sampled_blocks(oracle_lib):
+    """The 2048 x 2048 (L=16, k=2, T=256) workload at tau = 0.1: every block on the GPU,
+    8 sampled blocks (with both corners) through the oracle."""
+    w = wl.WORKLOADS[1]
+    import oracle
+    W = wl.make_weights(w)
+    C = oracle.make_codebook(w.L, w.V, w.codebook_seed)
+    _say("bcjr full 2048x2048: gpu")
+    soft, logz = _gpu(W, None, C, w.L, w.k, w.V, w.T, 0.1)
+    rng = np.random.default_rng(3)
+    blocks = np.unique(np.concatenate([rng.choice(w.blocks, 6, replace=False),
+                                       [0, w.blocks - 1]]))
+    _say(f"  oracle on blocks {blocks.tolist()}")
+    worst = _check(soft, logz, W, None, C, w.L, w.k, w.V, w.T, 0.1, blocks, threads=8)
+    _say(f"  worst error / tolerance {worst:.3f}")
+    assert np.all(np.isfinite(soft)) and np.all(np.isfinite(logz))

@@ -11,6 +11,8 @@ from ._lib import (  # noqa: F401
     tcq_decode_gemv,
     tcq_ldlq_workspace_bytes,
     tcq_encode_ldlq,
+    tcq_bcjr_workspace_bytes,
+    tcq_bcjr,
     tcq_encode,
     tcq_encode_timed,
     tcq_encode_workspace_bytes,

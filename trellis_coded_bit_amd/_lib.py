@@ -24,7 +24,8 @@ TCQ_ENOMEM = -5
 EXPORTED = ("tcq_version", "tcq_last_error", "tcq_make_codebook",
             "tcq_encode_workspace_bytes", "tcq_encode_workspace_min_bytes", "tcq_encode",
             "tcq_encode_timed", "tcq_decode", "tcq_decode_gemv",
-            "tcq_ldlq_workspace_bytes", "tcq_encode_ldlq")
+            "tcq_ldlq_workspace_bytes", "tcq_encode_ldlq", "tcq_bcjr_workspace_bytes",
+            "tcq_bcjr")
 
 _lib = None
 
@@ -71,6 +72,12 @@ def load():
     lib.tcq_encode_ldlq.restype = i32
     lib.tcq_encode_ldlq.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, i32, i32, i32, i32,
                                     vp, vp, vp, vp, i64, vp, i64, vp, sz, vp]
+    lib.tcq_bcjr_workspace_bytes.restype = i32
+    lib.tcq_bcjr_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32,
+                                             ctypes.POINTER(ctypes.c_size_t)]
+    lib.tcq_bcjr.restype = i32
+    lib.tcq_bcjr.argtypes = [vp, i64, i64, i64, vp, vp, i32, i32, i32, i32, ctypes.c_float,
+                             vp, i64, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -161,3 +168,18 @@ def tcq_encode_ldlq(W: int, M: int, N: int, ldw: int, U: int | None, ldu: int,
                                   T, bitstream, start_state, cost, recon or None, ldr,
                                   target or None, ldt, workspace, workspace_bytes,
                                   stream or None))
+
+
+def tcq_bcjr_workspace_bytes(M: int, N: int, L: int, k: int, V: int, T: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check("tcq_bcjr_workspace_bytes",
+           load().tcq_bcjr_workspace_bytes(M, N, L, k, V, T, ctypes.byref(b)))
+    return int(b.value)
+
+
+def tcq_bcjr(W: int, M: int, N: int, ldw: int, d: int | None, codebook: int, L: int, k: int,
+             V: int, T: int, tau: float, soft: int, ldo: int, logz: int | None, workspace: int,
+             workspace_bytes: int, stream: int | None) -> None:
+    _check("tcq_bcjr",
+           load().tcq_bcjr(W, M, N, ldw, d or None, codebook, L, k, V, T, tau, soft, ldo,
+                           logz or None, workspace, workspace_bytes, stream or None))

@@ -118,3 +118,21 @@ def encode_ldlq(W: torch.Tensor, U: torch.Tensor | None, d: torch.Tensor | None,
                          N, None if out.target is None else out.target.data_ptr(), N,
                          workspace.ptr, workspace.nbytes, _stream())
     return out
+
+
+def bcjr(W: torch.Tensor, d: torch.Tensor | None, codebook: torch.Tensor, L: int, k: int,
+         V: int, T: int, tau: float, workspace: Workspace | None = None
+         ) -> tuple[torch.Tensor, torch.Tensor]:
+    """Soft codewords (float32 [M, N]) and log Z per block (float32 [M*N/T])."""
+    assert W.is_cuda and W.dtype == torch.float32 and W.dim() == 2 and W.stride(1) == 1
+    M, N = W.shape
+    if d is not None:
+        assert d.is_cuda and d.dtype == torch.float32 and d.is_contiguous() and d.numel() == N
+    soft = torch.empty((M, N), dtype=torch.float32, device=W.device)
+    logz = torch.empty(M * (N // T), dtype=torch.float32, device=W.device)
+    if workspace is None:
+        workspace = Workspace(_lib.tcq_bcjr_workspace_bytes(M, N, L, k, V, T), W.device)
+    _lib.tcq_bcjr(W.data_ptr(), M, N, W.stride(0), None if d is None else d.data_ptr(),
+                  codebook.data_ptr(), L, k, V, T, float(tau), soft.data_ptr(), N,
+                  logz.data_ptr(), workspace.ptr, workspace.nbytes, _stream())
+    return soft, logz

@@ -1,0 +1,359 @@
+// Soft trellis (BCJR) at temperature tau.  BCJR-QAT abstract (aqora listing): the
+// Viterbi argmax is replaced by the BCJR forward-backward sum-product at a temperature;
+// the soft codeword is the Boltzmann expectation of the emitted values over all trellis
+// paths, and the hard code comes back as the temperature goes to 0.
+//
+// Energy of a path = the weighted squared error the Viterbi search minimises, with the
+// same fp32 branch metric chain; probability of a path = exp(-J/tau) / Z.  Work is in
+// base-2 logs: g(s) = m(s) * ns with ns = -log2(e)/tau.
+//
+// Group form used here (x = a group of 2^kv states that share predecessors):
+//  - forward:  F_t(x) = LSE_j [g_t(s_j) + F_{t-1}(s_j >> kv)], s_j = (j << (L-kv)) | x,
+//              F_0 = 0; then alpha_t(s') = g_t(s') + F_{t-1}(s' >> kv), and
+//              log2 Z = LSE_x F_n(x).
+//  - backward: the successors of s depend only on x = s mod 2^(L-kv), so
+//              beta_t(s) = B_t(s mod 2^(L-kv)) with B_n = 0 and
+//              B_{t-1}(x) = LSE_b [g_t(s'_b) + B_t(s'_b mod 2^(L-kv))], s'_b = (x << kv) | b.
+//  - marginal: P(s_t = s'_b) is proportional to 2^(g_t(s'_b) + B_t(..) + F_{t-1}(x)),
+//              i.e. a softmax over b inside the group times a group weight.
+// Only vectors of 2^(L-kv) values are carried (in LDS when they fit).  F_{t-1} is kept
+// in the workspace for the backward pass.  Each step's vector is shifted by the previous
+// step's maximum so values stay near 0; a per-step constant cancels in the marginals,
+// and the forward shifts are summed (in double) for log Z.
+#include <hip/hip_runtime.h>
+
+#include "tcq.h"
+#include "tcq_internal.h"
+
+namespace tcq {
+namespace {
+
+constexpr int kMaxThreads = 1024;
+constexpr int kMaxWaves = kMaxThreads / 64;
+constexpr float kNegInf = -__builtin_inff();
+
+struct BcjrArgs {
+    const float *W;
+    int64_t ldw;
+    const float *d;
+    const float *C;
+    int L, kv, V, n;
+    int64_t blocks_per_row, block0;
+    float ns;              // -log2(e) / tau
+    float *fstore;         // [block][t][x], t < n
+    int64_t fstore_per_block;
+    float *gbuf;           // 2 * 2^(L-kv) floats per block when the vectors are not in LDS
+    int64_t gbuf_per_block;
+    float *soft;
+    int64_t ldo;
+    float *logz;
+};
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float metric(const float *wv, const float *dv, const float *c, int V,
+                                        bool weighted) {
+    float acc = 0.0f;
+    for (int v = 0; v < V; ++v) {
+        const float e = wv[v] - c[v];
+        const float de = weighted ? dv[v] * e : e;
+        acc = __builtin_fmaf(de, e, acc);
+    }
+    return acc;
+}
+
+// (m, s) stands for m + log2(s); merge two such pairs.
+__device__ __forceinline__ void lse_merge(float &m, float &s, float om, float os) {
+    const float nm = fmaxf(m, om);
+    if (nm == kNegInf) return;
+    s = s * exp2_(m - nm) + os * exp2_(om - nm);
+    m = nm;
+}
+
+// Weighted expectation accumulator: (u, num[], den) stands for the pair
+// (2^u * num, 2^u * den).
+struct Expect {
+    float u;
+    float num[TCQ_MAX_V];
+    float den;
+};
+
+__device__ __forceinline__ void expect_merge(Expect &a, float ou, const float *onum, float oden,
+                                             int V) {
+    const float nm = fmaxf(a.u, ou);
+    if (nm == kNegInf) return;
+    const float sa = (a.u == kNegInf) ? 0.0f : exp2_(a.u - nm);
+    const float sb = (ou == kNegInf) ? 0.0f : exp2_(ou - nm);
+    for (int v = 0; v < V; ++v) a.num[v] = a.num[v] * sa + onum[v] * sb;
+    a.den = a.den * sa + oden * sb;
+    a.u = nm;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+// Threads per workgroup: 1024 for up to 4 terms per group, 512 above (more registers).
+constexpr int max_threads(int kv) { return kv <= 2 ? kMaxThreads : kMaxThreads / 2; }
+
+// G = 2^KV predecessors/successors per group, held in registers (KV <= 4).
+template <int KV, bool IN_LDS>
+__global__ __launch_bounds__(max_threads(KV)) void bcjr_kernel(BcjrArgs a) {
+    extern __shared__ float lds[];
+    __shared__ float part_max[2][kMaxWaves];
+    __shared__ float part_m[kMaxWaves], part_s[kMaxWaves];
+    __shared__ float part_u[2][kMaxWaves];
+    __shared__ float part_num[2][kMaxWaves][TCQ_MAX_V];
+    __shared__ float part_den[2][kMaxWaves];
+
+    constexpr int G = 1 << KV;
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nwaves = nt >> 6;
+    const int L = a.L;
+    const int V = a.V;
+    const int n = a.n;
+    const int64_t X = int64_t{1} << (L - KV);
+    const int sh = L - KV;
+    const int64_t blk = a.block0 + blockIdx.x;
+    const int64_t row = blk / a.blocks_per_row;
+    const int64_t col = blk % a.blocks_per_row;
+    const int T = n * V;
+    const float *w = a.W + row * a.ldw + col * T;
+    const float *dd = a.d ? a.d + col * T : nullptr;
+    const bool weighted = a.d != nullptr;
+    float *fst = a.fstore + static_cast<int64_t>(blockIdx.x) * a.fstore_per_block;
+    float *bufA = IN_LDS ? lds : a.gbuf + static_cast<int64_t>(blockIdx.x) * a.gbuf_per_block;
+    float *bufB = bufA + X;
+    const float ns = a.ns;
+
+    for (int64_t x = tid; x < X; x += nt) {
+        bufA[x] = 0.0f;
+        fst[x] = 0.0f;  // F_0
+    }
+    __syncthreads();
+
+    // ---------------- forward ----------------
+    float *Fc = bufA;
+    float *Fn = bufB;
+    double offset = 0.0;  // sum of the shifts, base-2 log
+    float wv[TCQ_MAX_V], dv[TCQ_MAX_V];
+    for (int t = 1; t <= n; ++t) {
+        float c = 0.0f;
+        if (t >= 2) {
+            c = part_max[(t - 1) & 1][0];
+            for (int i = 1; i < nwaves; ++i) c = fmaxf(c, part_max[(t - 1) & 1][i]);
+            offset += static_cast<double>(c);
+        }
+        for (int v = 0; v < V; ++v) {
+            wv[v] = w[(t - 1) * V + v];
+            dv[v] = weighted ? dd[(t - 1) * V + v] : 1.0f;
+        }
+        float lmax = kNegInf;
+        for (int64_t x = tid; x < X; x += nt) {
+            float val[G];
+            float mx = kNegInf;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int64_t s = (static_cast<int64_t>(j) << sh) | x;
+                val[j] = metric(wv, dv, a.C + s * V, V, weighted) * ns + Fc[s >> KV];
+                mx = fmaxf(mx, val[j]);
+            }
+            float sum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < G; ++j) sum += exp2_(val[j] - mx);
+            const float f = mx + log2_(sum) - c;
+            Fn[x] = f;
+            if (t < n) fst[static_cast<int64_t>(t) * X + x] = f;
+            lmax = fmaxf(lmax, f);
+        }
+        lmax = wave_max(lmax);
+        if (lane == 0) part_max[t & 1][wave] = lmax;
+        __syncthreads();
+        float *tmp = Fc;
+        Fc = Fn;
+        Fn = tmp;
+    }
+    // log2 Z = LSE_x F_n(x) + offset
+    {
+        float m = kNegInf, s = 0.0f;
+        for (int64_t x = tid; x < X; x += nt) lse_merge(m, s, Fc[x], 1.0f);
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float om = __shfl_xor(m, off);
+            const float os = __shfl_xor(s, off);
+            lse_merge(m, s, om, os);
+        }
+        if (lane == 0) {
+            part_m[wave] = m;
+            part_s[wave] = s;
+        }
+        __syncthreads();
+        if (tid == 0 && a.logz) {
+            float fm = part_m[0], fs = part_s[0];
+            for (int i = 1; i < nwaves; ++i) lse_merge(fm, fs, part_m[i], part_s[i]);
+            const double l2 = static_cast<double>(fm) + static_cast<double>(log2_(fs)) + offset;
+            a.logz[blk] = static_cast<float>(l2 * 0.69314718055994530942);
+        }
+    }
+    __threadfence();
+    __syncthreads();
+
+    // ---------------- backward ----------------
+    float *Bc = bufA;
+    float *Bn = bufB;
+    for (int64_t x = tid; x < X; x += nt) Bc[x] = 0.0f;
+    __syncthreads();
+    const int64_t lowmask = X - 1;
+    float *out = a.soft + row * a.ldo + col * T;
+    for (int t = n; t >= 1; --t) {
+        float c = 0.0f;
+        if (t < n) {
+            c = part_max[(t + 1) & 1][0];
+            for (int i = 1; i < nwaves; ++i) c = fmaxf(c, part_max[(t + 1) & 1][i]);
+        }
+        for (int v = 0; v < V; ++v) {
+            wv[v] = w[(t - 1) * V + v];
+            dv[v] = weighted ? dd[(t - 1) * V + v] : 1.0f;
+        }
+        Expect ex;
+        ex.u = kNegInf;
+        for (int v = 0; v < TCQ_MAX_V; ++v) ex.num[v] = 0.0f;
+        ex.den = 0.0f;
+        float lmax = kNegInf;
+        for (int64_t x = tid; x < X; x += nt) {
+            const float fx = fst[static_cast<int64_t>(t - 1) * X + x];
+            float val[G];
+            float mx = kNegInf;
+#pragma unroll
+            for (int b = 0; b < G; ++b) {
+                const int64_t s2 = (x << KV) | b;
+                val[b] = metric(wv, dv, a.C + s2 * V, V, weighted) * ns + Bc[s2 & lowmask];
+                mx = fmaxf(mx, val[b]);
+            }
+            float sum = 0.0f;
+            float gnum[TCQ_MAX_V];
+            for (int v = 0; v < V; ++v) gnum[v] = 0.0f;
+#pragma unroll
+            for (int b = 0; b < G; ++b) {
+                const float e = exp2_(val[b] - mx);
+                sum += e;
+                const float *cs = a.C + ((x << KV) | b) * V;
+                for (int v = 0; v < V; ++v) gnum[v] = __builtin_fmaf(e, cs[v], gnum[v]);
+            }
+            if (t > 1) {
+                const float bnew = mx + log2_(sum) - c;
+                Bn[x] = bnew;
+                lmax = fmaxf(lmax, bnew);
+            }
+            expect_merge(ex, mx + fx, gnum, sum, V);
+        }
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ou = __shfl_xor(ex.u, off);
+            float onum[TCQ_MAX_V];
+            for (int v = 0; v < V; ++v) onum[v] = __shfl_xor(ex.num[v], off);
+            const float oden = __shfl_xor(ex.den, off);
+            expect_merge(ex, ou, onum, oden, V);
+        }
+        lmax = wave_max(lmax);
+        if (lane == 0) {
+            part_max[t & 1][wave] = lmax;
+            part_u[t & 1][wave] = ex.u;
+            for (int v = 0; v < V; ++v) part_num[t & 1][wave][v] = ex.num[v];
+            part_den[t & 1][wave] = ex.den;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            Expect tot;
+            tot.u = part_u[t & 1][0];
+            for (int v = 0; v < V; ++v) tot.num[v] = part_num[t & 1][0][v];
+            tot.den = part_den[t & 1][0];
+            for (int i = 1; i < nwaves; ++i)
+                expect_merge(tot, part_u[t & 1][i], part_num[t & 1][i], part_den[t & 1][i], V);
+            for (int v = 0; v < V; ++v) out[(t - 1) * V + v] = tot.num[v] / tot.den;
+        }
+        float *tmp = Bc;
+        Bc = Bn;
+        Bn = tmp;
+    }
+}
+
+template <int KV, bool IN_LDS>
+hipError_t launch_kv(const BcjrArgs &a, int64_t nb, int threads, size_t shmem, hipStream_t s) {
+    auto kern = bcjr_kernel<KV, IN_LDS>;
+    if (threads > max_threads(KV)) threads = max_threads(KV);
+    if (shmem > 0) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(shmem));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nb)), dim3(threads), shmem, s, a);
+    return hipGetLastError();
+}
+
+template <bool IN_LDS>
+hipError_t launch_lds(const BcjrArgs &a, int64_t nb, int threads, size_t shmem, hipStream_t s) {
+    switch (a.kv) {
+        case 1: return launch_kv<1, IN_LDS>(a, nb, threads, shmem, s);
+        case 2: return launch_kv<2, IN_LDS>(a, nb, threads, shmem, s);
+        case 3: return launch_kv<3, IN_LDS>(a, nb, threads, shmem, s);
+        case 4: return launch_kv<4, IN_LDS>(a, nb, threads, shmem, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool bcjr_supported(int L, int kv) { return kv >= 1 && kv <= kBcjrMaxKV && kv < L && L <= 16; }
+
+bool bcjr_in_lds(int L, int kv) {
+    return (size_t{2} << (L - kv)) * sizeof(float) <= kBcjrLdsBytes;
+}
+
+size_t bcjr_per_block_bytes(int L, int kv, int n) {
+    const size_t X = size_t{1} << (L - kv);
+    size_t b = align_up(static_cast<size_t>(n) * X * sizeof(float), 256);
+    if (!bcjr_in_lds(L, kv)) b += align_up(2 * X * sizeof(float), 256);
+    return b;
+}
+
+hipError_t launch_bcjr(const float *W, int64_t ldw, const float *d, const float *C, int L, int k,
+                       int V, int T, int64_t blocks_per_row, int64_t block0, int64_t nb,
+                       float tau, char *ws, float *soft, int64_t ldo, float *logz,
+                       hipStream_t s) {
+    const int kv = k * V;
+    const int64_t X = int64_t{1} << (L - kv);
+    const int n = T / V;
+    BcjrArgs a{};
+    a.W = W;
+    a.ldw = ldw;
+    a.d = d;
+    a.C = C;
+    a.L = L;
+    a.kv = kv;
+    a.V = V;
+    a.n = n;
+    a.blocks_per_row = blocks_per_row;
+    a.block0 = block0;
+    a.ns = static_cast<float>(-1.4426950408889634074 / static_cast<double>(tau));
+    const bool in_lds = bcjr_in_lds(L, kv);
+    const size_t fbytes = align_up(static_cast<size_t>(n) * X * sizeof(float), 256);
+    a.fstore = reinterpret_cast<float *>(ws);
+    a.fstore_per_block = static_cast<int64_t>(bcjr_per_block_bytes(L, kv, n) / sizeof(float));
+    a.gbuf = in_lds ? nullptr : reinterpret_cast<float *>(ws + fbytes);
+    a.gbuf_per_block = a.fstore_per_block;
+    a.soft = soft;
+    a.ldo = ldo;
+    a.logz = logz;
+    int threads = static_cast<int>(X < kMaxThreads ? X : kMaxThreads);
+    threads = ((threads + 63) / 64) * 64;
+    const size_t shmem = in_lds ? 2 * static_cast<size_t>(X) * sizeof(float) : 0;
+    return in_lds ? launch_lds<true>(a, nb, threads, shmem, s)
+                  : launch_lds<false>(a, nb, threads, shmem, s);
+}
+
+}  // namespace tcq

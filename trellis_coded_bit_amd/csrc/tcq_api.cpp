@@ -1,6 +1,7 @@
 // libtcq C ABI: argument checks, workspace planning, and launch ordering on the
 // caller's stream.  Every numeric step runs in the HIP kernels.
 #include <cstdarg>
+#include <cmath>
 #include <cstdio>
 #include <string>
 
@@ -418,6 +419,83 @@ extern "C" int tcq_encode_ldlq(const float *W, int64_t M, int64_t N, int64_t ldw
                                    stream);
             if (e != hipSuccess) return hip_fail(fn, "feedback update launch", e);
         }
+    }
+    return TCQ_OK;
+}
+
+// Soft trellis (BCJR): workspace = per-block forward vectors for a batch of blocks.
+namespace {
+constexpr int64_t kBcjrRecommendedBytes = int64_t{8} << 30;
+
+int check_bcjr(const char *fn, int64_t M, int64_t N, int L, int k, int V, int T) {
+    int rc = check_trellis(fn, M, N, L, k, V, T);
+    if (rc != TCQ_OK) return rc;
+    if (!bcjr_supported(L, k * V)) {
+        set_error("%s: the soft trellis supports k*V <= %d (k=%d V=%d)", fn, kBcjrMaxKV, k, V);
+        return TCQ_EUNSUPPORTED;
+    }
+    return TCQ_OK;
+}
+}  // namespace
+
+extern "C" int tcq_bcjr_workspace_bytes(int64_t M, int64_t N, int L, int k, int V, int T,
+                                        size_t *bytes) {
+    clear_error();
+    const char *fn = "tcq_bcjr_workspace_bytes";
+    int rc = check_bcjr(fn, M, N, L, k, V, T);
+    if (rc != TCQ_OK) return rc;
+    if (!bytes) {
+        set_error("%s: bytes is NULL", fn);
+        return TCQ_EINVAL;
+    }
+    const size_t per = bcjr_per_block_bytes(L, k * V, T / V);
+    const int64_t nblocks = (T > 0 && N > 0) ? M * (N / T) : 0;
+    int64_t batch = kBcjrRecommendedBytes / static_cast<int64_t>(per);
+    if (batch > nblocks) batch = nblocks;
+    if (batch < 1) batch = 1;
+    *bytes = per * static_cast<size_t>(batch);
+    return TCQ_OK;
+}
+
+extern "C" int tcq_bcjr(const float *W, int64_t M, int64_t N, int64_t ldw, const float *d,
+                        const float *codebook, int L, int k, int V, int T, float tau,
+                        float *soft, int64_t ldo, float *logz, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    clear_error();
+    const char *fn = "tcq_bcjr";
+    int rc = check_bcjr(fn, M, N, L, k, V, T);
+    if (rc != TCQ_OK) return rc;
+    if (!(tau > 0.0f) || !std::isfinite(tau) ||
+        !std::isfinite(static_cast<float>(-1.4426950408889634074 / static_cast<double>(tau)))) {
+        set_error("%s: tau=%g must be positive, finite and not below 1e-38", fn, (double)tau);
+        return TCQ_EINVAL;
+    }
+    if (M == 0 || N == 0) return TCQ_OK;
+    if (!W || !codebook || !soft) {
+        set_error("%s: W, codebook and soft must be non-NULL", fn);
+        return TCQ_EINVAL;
+    }
+    if (ldw < N || ldo < N) {
+        set_error("%s: ldw=%lld and ldo=%lld must be >= N=%lld", fn, (long long)ldw,
+                  (long long)ldo, (long long)N);
+        return TCQ_EINVAL;
+    }
+    const size_t per = bcjr_per_block_bytes(L, k * V, T / V);
+    if (!workspace || workspace_bytes < per) {
+        set_error("%s: workspace of %zu bytes is below the minimum %zu", fn,
+                  workspace ? workspace_bytes : size_t{0}, per);
+        return TCQ_EWORKSPACE;
+    }
+    const int64_t bpr = N / T;
+    const int64_t nblocks = M * bpr;
+    int64_t batch = static_cast<int64_t>(workspace_bytes / per);
+    if (batch > nblocks) batch = nblocks;
+    if (batch > 0x7FFFFFFF) batch = 0x7FFFFFFF;
+    for (int64_t b0 = 0; b0 < nblocks; b0 += batch) {
+        const int64_t nb = (nblocks - b0 < batch) ? nblocks - b0 : batch;
+        hipError_t e = launch_bcjr(W, ldw, d, codebook, L, k, V, T, bpr, b0, nb, tau,
+                                   static_cast<char *>(workspace), soft, ldo, logz, stream);
+        if (e != hipSuccess) return hip_fail(fn, "soft-trellis launch", e);
     }
     return TCQ_OK;
 }

@@ -54,6 +54,17 @@ hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_s
                               const float *C, const float *x, float *y, int64_t M, int64_t N,
                               int L, int k, int V, int T, hipStream_t s);
 
+// Soft trellis (BCJR).
+constexpr int kBcjrMaxKV = 4;                    // 2^kv terms per group kept in registers
+constexpr size_t kBcjrLdsBytes = size_t{128} << 10;  // two group vectors in LDS up to this
+bool bcjr_supported(int L, int kv);
+bool bcjr_in_lds(int L, int kv);
+size_t bcjr_per_block_bytes(int L, int kv, int n);
+hipError_t launch_bcjr(const float *W, int64_t ldw, const float *d, const float *C, int L, int k,
+                       int V, int T, int64_t blocks_per_row, int64_t block0, int64_t nb,
+                       float tau, char *ws, float *soft, int64_t ldo, float *logz,
+                       hipStream_t s);
+
 // Error feedback over coding blocks.
 hipError_t launch_ldlq_update(float *tgt, int64_t ldt, const float *W, int64_t ldw,
                               const float *what, int64_t ldh, const float *U, int64_t ldu,
