@@ -20,4 +20,6 @@ from .oracle import (  # noqa: F401
     ldlq_encode,
     bcjr_block,
     bcjr_matrix,
+    hadamard,
+    scale_field,
 )

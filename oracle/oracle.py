@@ -19,6 +19,7 @@ _LIB = os.path.join(_HERE, "libtcq_oracle.so")
 
 _f32p = ctypes.POINTER(ctypes.c_float)
 _u32p = ctypes.POINTER(ctypes.c_uint32)
+_f64p = ctypes.POINTER(ctypes.c_double)
 _lib = None
 
 
@@ -67,11 +68,16 @@ def _load():
     lib.oracle_ldlq_row.argtypes = [_f32p, _f32p, ctypes.c_long, _f32p, _f32p, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_long,
                                     _u32p, _u32p, _f32p, _f32p, _f32p]
-    _f64p = ctypes.POINTER(ctypes.c_double)
     lib.oracle_bcjr_block.restype = ctypes.c_int
     lib.oracle_bcjr_block.argtypes = [_f64p, _f64p, _f32p, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_double, _f64p,
                                       _f64p]
+    lib.oracle_hadamard_row.restype = ctypes.c_int
+    lib.oracle_hadamard_row.argtypes = [_f64p, ctypes.c_long, ctypes.c_long, _f64p,
+                                        ctypes.c_int, _f64p]
+    lib.oracle_scale_field.restype = ctypes.c_int
+    lib.oracle_scale_field.argtypes = [_f32p, ctypes.c_long, ctypes.c_long, ctypes.c_long,
+                                       _f64p, _f64p, _f64p]
     _lib = lib
     return lib
 
@@ -302,3 +308,39 @@ def bcjr_matrix(W, d, C, L, k, V, T, tau, blocks=None, threads=1):
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(one, range(blocks.size)))
     return soft, logz
+
+
+def hadamard(X, n, sigma=None, inverse=False):
+    """Rows of X rotated by R = H_n diag(sigma) / sqrt(n) in chunks of n (inverse: R^T).
+    float64 result."""
+    f64p = ctypes.POINTER(ctypes.c_double)
+    X = np.atleast_2d(np.asarray(X, dtype=np.float64))
+    rows, length = X.shape
+    sg = None if sigma is None else np.ascontiguousarray(sigma, dtype=np.float64)
+    out = np.empty_like(X)
+    lib = _load()
+    for r in range(rows):
+        xr = np.ascontiguousarray(X[r])
+        yr = np.empty(length, dtype=np.float64)
+        rc = lib.oracle_hadamard_row(xr.ctypes.data_as(f64p), length, n,
+                                     None if sg is None else sg.ctypes.data_as(f64p),
+                                     1 if inverse else 0, yr.ctypes.data_as(f64p))
+        if rc != 0:
+            raise ValueError(f"oracle_hadamard_row failed ({rc})")
+        out[r] = yr
+    return out
+
+
+def scale_field(W):
+    """(a [M], b [N], Wn [M, N]) in float64 with W = a_r b_c Wn_rc."""
+    f64p = ctypes.POINTER(ctypes.c_double)
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    M, N = W.shape
+    a = np.empty(M, dtype=np.float64)
+    b = np.empty(N, dtype=np.float64)
+    Wn = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_scale_field(_fp(W), M, N, N, a.ctypes.data_as(f64p),
+                                    b.ctypes.data_as(f64p), Wn.ctypes.data_as(f64p))
+    if rc != 0:
+        raise ValueError(f"oracle_scale_field failed ({rc})")
+    return a, b, Wn

@@ -31,6 +31,8 @@
  *
  * Error feedback (LDLQ) over coding blocks: oracle_ldlq_row, with its own note below.
  * Soft trellis (BCJR) at a temperature: oracle_bcjr_block, with its own note below.
+ * Pre-processing: oracle_hadamard_row (randomized Hadamard rotation) and
+ * oracle_scale_field (factored scale field), with their own notes below.
  *
  * Build: gcc -O2 -std=c99 -ffp-contract=off -fPIC -shared (no fast-math).
  */
@@ -600,6 +602,81 @@ int oracle_bcjr_block(const double *w, const double *d, const float *C, int L, i
     free(a);
     free(b);
     free(bn);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Randomized Hadamard rotation.  Pingala-8 post, rotation paragraph and its   */
+/* 4x4 example: with R orthogonal, W x = (W R^T)(R x); the usual R is a        */
+/* Hadamard matrix with random signs, scaled to be orthogonal.  Reading: R =   */
+/* H_n diag(sigma) / sqrt(n) with H_n the Sylvester-ordered Hadamard matrix,   */
+/* H_n[k][i] = (-1)^popcount(k & i) (the page's 4x4 example is H_4 / 2).  A    */
+/* row longer than n is rotated in consecutive chunks of n (block diagonal R). */
+/* Forward: y = R x, i.e. y_k = sum_i H[k][i] sigma_i x_i / sqrt(n).           */
+/* Inverse: x = R^T y, i.e. x_i = sigma_i sum_k H[i][k] y_k / sqrt(n).         */
+/* Plain O(n^2) sums in double.                                                */
+/* ------------------------------------------------------------------------- */
+static int popcount_long(unsigned long v)
+{
+    int c = 0;
+    while (v) {
+        c += (int)(v & 1u);
+        v >>= 1;
+    }
+    return c;
+}
+
+int oracle_hadamard_row(const double *x, long len, long n, const double *sigma, int inverse,
+                        double *y)
+{
+    if (n < 1 || (n & (n - 1)) != 0 || len % n != 0)
+        return ORACLE_EINVAL;
+    const double scale = 1.0 / sqrt((double)n);
+    for (long base = 0; base < len; base += n) {
+        for (long k = 0; k < n; ++k) {
+            double acc = 0.0;
+            for (long i = 0; i < n; ++i) {
+                const double h = (popcount_long((unsigned long)(k & i)) & 1) ? -1.0 : 1.0;
+                const double xi = x[base + i] * ((!inverse && sigma) ? sigma[base + i] : 1.0);
+                acc += h * xi;
+            }
+            y[base + k] = acc * scale * ((inverse && sigma) ? sigma[base + k] : 1.0);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Factored row x column scale field.  CurveTQ abstract: no rotation; the      */
+/* weights' amplitude is carried by a factored (row times column) scale field. */
+/* Reading: one closed-form pass each way,                                     */
+/*   a_r = sqrt(mean_c W_rc^2),   b_c = sqrt(mean_r (W_rc / a_r)^2),           */
+/* and W = a_r b_c Wn_rc.  Every column of Wn then has unit RMS.  A zero row   */
+/* or column gets scale 1.  Double precision.                                  */
+/* ------------------------------------------------------------------------- */
+int oracle_scale_field(const float *W, long M, long N, long ldw, double *a, double *b,
+                       double *Wn)
+{
+    if (M < 0 || N < 0 || ldw < N)
+        return ORACLE_EINVAL;
+    for (long r = 0; r < M; ++r) {
+        double s = 0.0;
+        for (long c = 0; c < N; ++c)
+            s += (double)W[r * ldw + c] * (double)W[r * ldw + c];
+        a[r] = (s > 0.0) ? sqrt(s / (double)N) : 1.0;
+    }
+    for (long c = 0; c < N; ++c) {
+        double s = 0.0;
+        for (long r = 0; r < M; ++r) {
+            const double v = (double)W[r * ldw + c] / a[r];
+            s += v * v;
+        }
+        b[c] = (s > 0.0) ? sqrt(s / (double)M) : 1.0;
+    }
+    if (Wn)
+        for (long r = 0; r < M; ++r)
+            for (long c = 0; c < N; ++c)
+                Wn[r * N + c] = (double)W[r * ldw + c] / (a[r] * b[c]);
     return ORACLE_OK;
 }
 
