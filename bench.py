@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--cpu-threads", type=int, default=0, help="0: min(16, cpu count)")
     ap.add_argument("--gemv-iters", type=int, default=200,
                     help="calls of the fused decode+GEMV timed after the encoder (0: skip)")
+    ap.add_argument("--preprocess-iters", type=int, default=100,
+                    help="timed calls of the Hadamard and scale-field kernels (0: skip)")
     ap.add_argument("--bcjr-tau", type=float, default=0.1,
                     help="temperature of the timed soft-trellis run (0: skip)")
     ap.add_argument("--ldlq-workload", type=int, default=2,
@@ -203,6 +205,47 @@ def bcjr_bench(torch, _lib, w, Wt, dt_, Ct, tau, steps):
             "state_updates_per_s_per_pass": updates / (ms / 1e3)}
 
 
+def preprocess_bench(torch, _lib, w, Wt, iters):
+    """Randomized Hadamard rotation (full row length when it is a power of two <= 4096,
+    else chunks of 2048) and the factored scale field, on the bench workload's W.
+    Algorithmic bytes: one read and one write of W (8 B per weight)."""
+    from trellis_coded_bit_amd import api
+    n = w.N if (w.N & (w.N - 1)) == 0 and w.N <= 4096 else 2048
+    g = torch.Generator(device="cpu").manual_seed(5)
+    sigma = (torch.randint(0, 2, (w.N,), generator=g).float() * 2 - 1).to(Wt.device)
+    Y = torch.empty_like(Wt)
+    a = torch.empty(w.M, dtype=torch.float32, device=Wt.device)
+    b = torch.empty(w.N, dtype=torch.float32, device=Wt.device)
+    ws = api.Workspace(_lib.tcq_scale_field_workspace_bytes(w.M, w.N), Wt.device)
+    stream = torch.cuda.current_stream()
+
+    def had():
+        _lib.tcq_hadamard(Wt.data_ptr(), w.M, w.N, w.N, n, sigma.data_ptr(), False,
+                          Y.data_ptr(), w.N, stream.cuda_stream)
+
+    def sf():
+        _lib.tcq_scale_field(Wt.data_ptr(), w.M, w.N, w.N, a.data_ptr(), b.data_ptr(),
+                             Y.data_ptr(), w.N, ws.ptr, ws.nbytes, stream.cuda_stream)
+
+    out = {}
+    for name, fn in (("hadamard", had), ("scale_field", sf)):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        nbytes = 8 * w.weights
+        gbps = nbytes / (us / 1e6) / 1e9
+        out[name] = {"us": us, "algorithmic_bytes": nbytes, "achieved_GBps": gbps,
+                     "frac_hbm": gbps / HBM_PEAK_GBPS}
+    out["hadamard"]["n"] = n
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -310,6 +353,9 @@ def main():
         log(f"[bench] fused decode+GEMV on the encoded matrix, {args.gemv_iters} calls",
             args.quiet)
         result["decode_gemv"] = gemv_bench(torch, _lib, w, out, Ct, args.gemv_iters)
+    if args.preprocess_iters > 0:
+        log("[bench] pre-processing kernels", args.quiet)
+        result["preprocess"] = preprocess_bench(torch, _lib, w, Wt, args.preprocess_iters)
     if args.bcjr_tau > 0:
         log(f"[bench] soft trellis at tau={args.bcjr_tau}", args.quiet)
         result["bcjr"] = bcjr_bench(torch, _lib, w, Wt, dt_, Ct, args.bcjr_tau, 1)

@@ -229,6 +229,41 @@ int tcq_bcjr(const float *W, int64_t M, int64_t N, int64_t ldw, const float *d,
              int64_t ldo, float *logz, void *workspace, size_t workspace_bytes,
              hipStream_t stream);
 
+/*
+ * tcq_hadamard -- randomized Hadamard rotation of rows (Pingala-8 post, rotation paragraph
+ * and its 4x4 example: W x = (W R^T)(R x) for orthogonal R, usually a Hadamard matrix
+ * with random signs).  R = H_n diag(sigma) / sqrt(n), H_n Sylvester-ordered
+ * (H_n[k][i] = (-1)^popcount(k & i)); rows longer than n are rotated in consecutive
+ * chunks of n (block-diagonal R).  Forward: each row x becomes R x (for the rows of W this
+ * is W R^T); inverse: R^T y.
+ *   X, ldx     : device, rows x len input
+ *   n          : power of two, n <= 4096; n divides len; if n < 64 then len <= 8192
+ *   sigma      : device, len floats (+1/-1), or NULL for all +1
+ *   Y, ldy     : device output; Y == X (with ldy == ldx) works in place
+ * fp32 butterflies; |error| <= (log2(n) + 2) u sum|x_i| / sqrt(n) per output.
+ * Errors: TCQ_EINVAL, TCQ_EUNSUPPORTED, TCQ_EHIP.
+ */
+int tcq_hadamard(const float *X, int64_t rows, int64_t len, int64_t ldx, int64_t n,
+                 const float *sigma, int inverse, float *Y, int64_t ldy, hipStream_t stream);
+
+/*
+ * tcq_scale_field -- factored row x column scale field (CurveTQ abstract: the weights'
+ * amplitude is carried by a factored scale field, with no rotation).  One closed-form pass
+ * each way: a_r = sqrt(mean_c W_rc^2), b_c = sqrt(mean_r (W_rc / a_r)^2), and
+ * Wn_rc = W_rc / (a_r b_c), so W = a_r b_c Wn_rc and every column of Wn has unit RMS.
+ * An all-zero row or column gets scale 1.
+ *   W, M, N, ldw : device input
+ *   row_scale    : device out, M floats (a); col_scale: device out, N floats (b)
+ *   Wn, ldn      : nullable device out, M x ldn
+ *   workspace    : device, >= tcq_scale_field_workspace_bytes(M, N)
+ * fp32 sums in a fixed order (deterministic).
+ * Errors: TCQ_EINVAL, TCQ_EUNSUPPORTED, TCQ_EWORKSPACE, TCQ_EHIP.
+ */
+int tcq_scale_field_workspace_bytes(int64_t M, int64_t N, size_t *bytes);
+int tcq_scale_field(const float *W, int64_t M, int64_t N, int64_t ldw, float *row_scale,
+                    float *col_scale, float *Wn, int64_t ldn, void *workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,9 @@ from ._lib import (  # noqa: F401
     tcq_encode_ldlq,
     tcq_bcjr_workspace_bytes,
     tcq_bcjr,
+    tcq_hadamard,
+    tcq_scale_field_workspace_bytes,
+    tcq_scale_field,
     tcq_encode,
     tcq_encode_timed,
     tcq_encode_workspace_bytes,

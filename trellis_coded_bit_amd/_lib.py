@@ -25,7 +25,7 @@ EXPORTED = ("tcq_version", "tcq_last_error", "tcq_make_codebook",
             "tcq_encode_workspace_bytes", "tcq_encode_workspace_min_bytes", "tcq_encode",
             "tcq_encode_timed", "tcq_decode", "tcq_decode_gemv",
             "tcq_ldlq_workspace_bytes", "tcq_encode_ldlq", "tcq_bcjr_workspace_bytes",
-            "tcq_bcjr")
+            "tcq_bcjr", "tcq_hadamard", "tcq_scale_field_workspace_bytes", "tcq_scale_field")
 
 _lib = None
 
@@ -78,6 +78,12 @@ def load():
     lib.tcq_bcjr.restype = i32
     lib.tcq_bcjr.argtypes = [vp, i64, i64, i64, vp, vp, i32, i32, i32, i32, ctypes.c_float,
                              vp, i64, vp, vp, sz, vp]
+    lib.tcq_hadamard.restype = i32
+    lib.tcq_hadamard.argtypes = [vp, i64, i64, i64, i64, vp, i32, vp, i64, vp]
+    lib.tcq_scale_field_workspace_bytes.restype = i32
+    lib.tcq_scale_field_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.tcq_scale_field.restype = i32
+    lib.tcq_scale_field.argtypes = [vp, i64, i64, i64, vp, vp, vp, i64, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -183,3 +189,25 @@ def tcq_bcjr(W: int, M: int, N: int, ldw: int, d: int | None, codebook: int, L: 
     _check("tcq_bcjr",
            load().tcq_bcjr(W, M, N, ldw, d or None, codebook, L, k, V, T, tau, soft, ldo,
                            logz or None, workspace, workspace_bytes, stream or None))
+
+
+def tcq_hadamard(X: int, rows: int, length: int, ldx: int, n: int, sigma: int | None,
+                 inverse: bool, Y: int, ldy: int, stream: int | None) -> None:
+    _check("tcq_hadamard",
+           load().tcq_hadamard(X, rows, length, ldx, n, sigma or None, 1 if inverse else 0, Y,
+                               ldy, stream or None))
+
+
+def tcq_scale_field_workspace_bytes(M: int, N: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check("tcq_scale_field_workspace_bytes",
+           load().tcq_scale_field_workspace_bytes(M, N, ctypes.byref(b)))
+    return int(b.value)
+
+
+def tcq_scale_field(W: int, M: int, N: int, ldw: int, row_scale: int, col_scale: int,
+                    Wn: int | None, ldn: int, workspace: int, workspace_bytes: int,
+                    stream: int | None) -> None:
+    _check("tcq_scale_field",
+           load().tcq_scale_field(W, M, N, ldw, row_scale, col_scale, Wn or None, ldn,
+                                  workspace, workspace_bytes, stream or None))

@@ -136,3 +136,32 @@ def bcjr(W: torch.Tensor, d: torch.Tensor | None, codebook: torch.Tensor, L: int
                   codebook.data_ptr(), L, k, V, T, float(tau), soft.data_ptr(), N,
                   logz.data_ptr(), workspace.ptr, workspace.nbytes, _stream())
     return soft, logz
+
+
+def hadamard(X: torch.Tensor, n: int, sigma: torch.Tensor | None = None, inverse: bool = False,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows of X rotated by R = H_n diag(sigma)/sqrt(n) in chunks of n (inverse: R^T)."""
+    assert X.is_cuda and X.dtype == torch.float32 and X.dim() == 2 and X.stride(1) == 1
+    rows, length = X.shape
+    if sigma is not None:
+        assert sigma.is_cuda and sigma.dtype == torch.float32 and sigma.is_contiguous()
+    if out is None:
+        out = torch.empty_like(X)
+    _lib.tcq_hadamard(X.data_ptr(), rows, length, X.stride(0), n,
+                      None if sigma is None else sigma.data_ptr(), inverse, out.data_ptr(),
+                      out.stride(0), _stream())
+    return out
+
+
+def scale_field(W: torch.Tensor, normalized: bool = True
+                ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor | None]:
+    """(row_scale [M], col_scale [N], Wn [M, N] or None) with W = a_r b_c Wn_rc."""
+    assert W.is_cuda and W.dtype == torch.float32 and W.dim() == 2 and W.stride(1) == 1
+    M, N = W.shape
+    a = torch.empty(M, dtype=torch.float32, device=W.device)
+    b = torch.empty(N, dtype=torch.float32, device=W.device)
+    Wn = torch.empty_like(W) if normalized else None
+    ws = Workspace(_lib.tcq_scale_field_workspace_bytes(M, N), W.device)
+    _lib.tcq_scale_field(W.data_ptr(), M, N, W.stride(0), a.data_ptr(), b.data_ptr(),
+                         None if Wn is None else Wn.data_ptr(), N, ws.ptr, ws.nbytes, _stream())
+    return a, b, Wn

@@ -1,0 +1,223 @@
+// Pre-processing before coding.
+//
+// Randomized Hadamard rotation (Pingala-8 post, rotation paragraph and its 4x4 example):
+// W x = (W R^T)(R x) for orthogonal R, with R = H_n diag(sigma) / sqrt(n) and H_n the
+// Sylvester-ordered Hadamard matrix, H_n[k][i] = (-1)^popcount(k & i).  Rows longer than
+// n are rotated in consecutive chunks of n.  Applied to a row x (forward, y = R x):
+// sign flip, then the fast Walsh-Hadamard butterflies (a, b) -> (a + b, a - b) over each
+// index bit, then the 1/sqrt(n) scale.  Inverse (x = R^T y): butterflies, scale, sign.
+//
+// Factored row x column scale field (CurveTQ abstract: amplitude carried by a factored
+// scale field instead of a rotation): a_r = sqrt(mean_c W_rc^2),
+// b_c = sqrt(mean_r (W_rc / a_r)^2), Wn_rc = W_rc / (a_r b_c); an all-zero row or column
+// gets scale 1.
+#include <hip/hip_runtime.h>
+
+#include "tcq.h"
+#include "tcq_internal.h"
+
+namespace tcq {
+namespace {
+
+// One wave per chunk of n = 64 * E values.  Element i = j * 64 + lane sits in register
+// j of lane `lane`: index bits 0..5 are lanes (butterflies through cross-lane shuffles),
+// bits 6.. are registers (butterflies inside the lane).  Loads and stores are 256-byte
+// rows per instruction.
+template <int E>
+__global__ __launch_bounds__(256) void fwht_wave_kernel(
+    const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
+    int64_t rows, int64_t chunks_per_row, const float *__restrict__ sigma, int inverse,
+    float scale) {
+    constexpr int n = 64 * E;
+    const int lane = threadIdx.x & 63;
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (chunk >= rows * chunks_per_row) return;
+    const int64_t r = chunk / chunks_per_row;
+    const int64_t c0 = (chunk % chunks_per_row) * n;
+    const float *x = X + r * ldx + c0;
+    const float *sg = sigma ? sigma + c0 : nullptr;
+    float v[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        v[j] = x[j * 64 + lane];
+        if (sg && !inverse) v[j] *= sg[j * 64 + lane];
+    }
+    // register bits (h = 64, 128, ...)
+#pragma unroll
+    for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            if ((j & h) == 0) {
+                const float a = v[j];
+                const float b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+    // lane bits (h = 1, ..., 32)
+#pragma unroll
+    for (int p = 1; p < 64; p <<= 1) {
+        const bool upper = (lane & p) != 0;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const float o = __shfl_xor(v[j], p);
+            v[j] = upper ? o - v[j] : v[j] + o;
+        }
+    }
+    float *y = Y + r * ldy + c0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        float t = v[j] * scale;
+        if (sg && inverse) t *= sg[j * 64 + lane];
+        y[j * 64 + lane] = t;
+    }
+}
+
+// Small chunks (n < 64): one workgroup of 64 threads per row, the row staged in LDS and
+// one barrier per butterfly level.
+__global__ __launch_bounds__(64) void fwht_small_kernel(
+    const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy, int64_t len,
+    int n, const float *__restrict__ sigma, int inverse, float scale) {
+    extern __shared__ float buf[];
+    const int64_t r = blockIdx.x;
+    const float *x = X + r * ldx;
+    for (int64_t i = threadIdx.x; i < len; i += 64) {
+        float t = x[i];
+        if (sigma && !inverse) t *= sigma[i];
+        buf[i] = t;
+    }
+    __syncthreads();
+    for (int h = 1; h < n; h <<= 1) {
+        for (int64_t q = threadIdx.x; q < len / 2; q += 64) {
+            // q-th pair of this level: low index has bit h clear
+            const int64_t lo = (q / h) * 2 * h + (q % h);
+            const float a = buf[lo];
+            const float b = buf[lo + h];
+            buf[lo] = a + b;
+            buf[lo + h] = a - b;
+        }
+        __syncthreads();
+    }
+    float *y = Y + r * ldy;
+    for (int64_t i = threadIdx.x; i < len; i += 64) {
+        float t = buf[i] * scale;
+        if (sigma && inverse) t *= sigma[i];
+        y[i] = t;
+    }
+}
+
+__global__ __launch_bounds__(256) void row_rms_kernel(const float *__restrict__ W, int64_t ldw,
+                                                      int64_t N, float *__restrict__ a) {
+    __shared__ float part[4];
+    const int64_t r = blockIdx.x;
+    const float *w = W + r * ldw;
+    float s = 0.0f;
+    for (int64_t c = threadIdx.x; c < N; c += 256) s = __builtin_fmaf(w[c], w[c], s);
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+        a[r] = tot > 0.0f ? __builtin_sqrtf(tot / static_cast<float>(N)) : 1.0f;
+    }
+}
+
+// Column sums of (W_rc / a_r)^2 over row slab blockIdx.y, rows in ascending order.
+__global__ __launch_bounds__(256) void col_partial_kernel(
+    const float *__restrict__ W, int64_t ldw, int64_t M, int64_t N, int64_t slab_rows,
+    const float *__restrict__ a, float *__restrict__ part) {
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (c >= N) return;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * slab_rows;
+    const int64_t r1 = (r0 + slab_rows < M) ? r0 + slab_rows : M;
+    float s = 0.0f;
+    for (int64_t r = r0; r < r1; ++r) {
+        const float v = W[r * ldw + c] / a[r];
+        s = __builtin_fmaf(v, v, s);
+    }
+    part[static_cast<int64_t>(blockIdx.y) * N + c] = s;
+}
+
+__global__ __launch_bounds__(256) void col_finalize_kernel(const float *__restrict__ part,
+                                                           int nslabs, int64_t M, int64_t N,
+                                                           float *__restrict__ b) {
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (c >= N) return;
+    float s = 0.0f;
+    for (int i = 0; i < nslabs; ++i) s += part[static_cast<int64_t>(i) * N + c];
+    b[c] = s > 0.0f ? __builtin_sqrtf(s / static_cast<float>(M)) : 1.0f;
+}
+
+__global__ __launch_bounds__(256) void scale_apply_kernel(
+    const float *__restrict__ W, int64_t ldw, int64_t N, const float *__restrict__ a,
+    const float *__restrict__ b, float *__restrict__ Wn, int64_t ldn) {
+    const int64_t r = blockIdx.x;
+    const float ar = a[r];
+    for (int64_t c = static_cast<int64_t>(blockIdx.y) * 256 + threadIdx.x; c < N;
+         c += static_cast<int64_t>(gridDim.y) * 256)
+        Wn[r * ldn + c] = W[r * ldw + c] / (ar * b[c]);
+}
+
+template <int E>
+hipError_t launch_wave(const float *X, int64_t ldx, float *Y, int64_t ldy, int64_t rows,
+                       int64_t cpr, const float *sigma, int inverse, float scale,
+                       hipStream_t s) {
+    const int64_t chunks = rows * cpr;
+    const int64_t grid = (chunks + 3) / 4;
+    hipLaunchKernelGGL(fwht_wave_kernel<E>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                       X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t scale_field_slabs(int64_t M) { return static_cast<size_t>(M < 64 ? (M > 0 ? M : 1) : 64); }
+
+hipError_t launch_hadamard(const float *X, int64_t ldx, float *Y, int64_t ldy, int64_t rows,
+                           int64_t len, int64_t n, const float *sigma, int inverse,
+                           hipStream_t s) {
+    const float scale = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(n)));
+    const int64_t cpr = len / n;
+    switch (n) {
+        case 64: return launch_wave<1>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+        case 128: return launch_wave<2>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+        case 256: return launch_wave<4>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+        case 512: return launch_wave<8>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+        case 1024: return launch_wave<16>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+        case 2048: return launch_wave<32>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+        case 4096: return launch_wave<64>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+        default: break;
+    }
+    // n < 64: whole row in LDS (len <= kHadamardSmallMaxLen)
+    const size_t shmem = static_cast<size_t>(len) * sizeof(float);
+    hipLaunchKernelGGL(fwht_small_kernel, dim3(static_cast<unsigned>(rows)), dim3(64), shmem, s,
+                       X, ldx, Y, ldy, len, static_cast<int>(n), sigma, inverse, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_field(const float *W, int64_t ldw, int64_t M, int64_t N, float *a,
+                              float *b, float *Wn, int64_t ldn, float *part, hipStream_t s) {
+    hipLaunchKernelGGL(row_rms_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, s, W, ldw,
+                       N, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nslabs = static_cast<int64_t>(scale_field_slabs(M));
+    const int64_t slab_rows = (M + nslabs - 1) / nslabs;
+    const int64_t cb = (N + 255) / 256;
+    hipLaunchKernelGGL(col_partial_kernel, dim3(static_cast<unsigned>(cb),
+                       static_cast<unsigned>(nslabs)), dim3(256), 0, s, W, ldw, M, N, slab_rows,
+                       a, part);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(col_finalize_kernel, dim3(static_cast<unsigned>(cb)), dim3(256), 0, s,
+                       part, static_cast<int>(nslabs), M, N, b);
+    e = hipGetLastError();
+    if (e != hipSuccess || !Wn) return e;
+    const int64_t gy = cb < 16 ? cb : 16;
+    hipLaunchKernelGGL(scale_apply_kernel, dim3(static_cast<unsigned>(M),
+                       static_cast<unsigned>(gy)), dim3(256), 0, s, W, ldw, N, a, b, Wn, ldn);
+    return hipGetLastError();
+}
+
+}  // namespace tcq

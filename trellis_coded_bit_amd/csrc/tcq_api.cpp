@@ -499,3 +499,81 @@ extern "C" int tcq_bcjr(const float *W, int64_t M, int64_t N, int64_t ldw, const
     }
     return TCQ_OK;
 }
+
+extern "C" int tcq_hadamard(const float *X, int64_t rows, int64_t len, int64_t ldx, int64_t n,
+                            const float *sigma, int inverse, float *Y, int64_t ldy,
+                            hipStream_t stream) {
+    clear_error();
+    const char *fn = "tcq_hadamard";
+    if (rows < 0 || len < 0 || n < 1 || (n & (n - 1)) != 0) {
+        set_error("%s: rows=%lld, len=%lld must be >= 0 and n=%lld a power of two", fn,
+                  (long long)rows, (long long)len, (long long)n);
+        return TCQ_EINVAL;
+    }
+    if (len % n != 0) {
+        set_error("%s: len=%lld is not a multiple of n=%lld", fn, (long long)len, (long long)n);
+        return TCQ_EINVAL;
+    }
+    if (n > kHadamardMaxN || (n < 64 && len > kHadamardSmallMaxLen)) {
+        set_error("%s: n=%lld above %lld, or len=%lld above %lld with n < 64", fn,
+                  (long long)n, (long long)kHadamardMaxN, (long long)len,
+                  (long long)kHadamardSmallMaxLen);
+        return TCQ_EUNSUPPORTED;
+    }
+    if (rows == 0 || len == 0) return TCQ_OK;
+    if (!X || !Y || ldx < len || ldy < len) {
+        set_error("%s: X and Y must be non-NULL with ldx, ldy >= len", fn);
+        return TCQ_EINVAL;
+    }
+    if (X != Y && ((X < Y + rows * ldy) && (Y < X + rows * ldx))) {
+        set_error("%s: X and Y overlap without being the same buffer", fn);
+        return TCQ_EINVAL;
+    }
+    if (X == Y && ldx != ldy) {
+        set_error("%s: in place needs ldx == ldy", fn);
+        return TCQ_EINVAL;
+    }
+    hipError_t e = launch_hadamard(X, ldx, Y, ldy, rows, len, n, sigma, inverse ? 1 : 0, stream);
+    if (e != hipSuccess) return hip_fail(fn, "Hadamard launch", e);
+    return TCQ_OK;
+}
+
+extern "C" int tcq_scale_field_workspace_bytes(int64_t M, int64_t N, size_t *bytes) {
+    clear_error();
+    if (M < 0 || N < 0 || !bytes) {
+        set_error("tcq_scale_field_workspace_bytes: negative size or NULL bytes");
+        return TCQ_EINVAL;
+    }
+    *bytes = scale_field_slabs(M) * static_cast<size_t>(N) * sizeof(float);
+    return TCQ_OK;
+}
+
+extern "C" int tcq_scale_field(const float *W, int64_t M, int64_t N, int64_t ldw,
+                               float *row_scale, float *col_scale, float *Wn, int64_t ldn,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    clear_error();
+    const char *fn = "tcq_scale_field";
+    if (M < 0 || N < 0) {
+        set_error("%s: negative size", fn);
+        return TCQ_EINVAL;
+    }
+    if (M == 0 || N == 0) return TCQ_OK;
+    if (!W || !row_scale || !col_scale || ldw < N || (Wn && ldn < N)) {
+        set_error("%s: W, row_scale, col_scale must be non-NULL, ldw >= N, ldn >= N", fn);
+        return TCQ_EINVAL;
+    }
+    if (M > 0x7FFFFFFF) {
+        set_error("%s: M=%lld rows exceed one launch", fn, (long long)M);
+        return TCQ_EUNSUPPORTED;
+    }
+    const size_t need = scale_field_slabs(M) * static_cast<size_t>(N) * sizeof(float);
+    if (!workspace || workspace_bytes < need) {
+        set_error("%s: workspace of %zu bytes is below %zu", fn,
+                  workspace ? workspace_bytes : size_t{0}, need);
+        return TCQ_EWORKSPACE;
+    }
+    hipError_t e = launch_scale_field(W, ldw, M, N, row_scale, col_scale, Wn, ldn,
+                                      static_cast<float *>(workspace), stream);
+    if (e != hipSuccess) return hip_fail(fn, "scale-field launch", e);
+    return TCQ_OK;
+}

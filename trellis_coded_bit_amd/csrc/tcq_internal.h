@@ -65,6 +65,16 @@ hipError_t launch_bcjr(const float *W, int64_t ldw, const float *d, const float 
                        float tau, char *ws, float *soft, int64_t ldo, float *logz,
                        hipStream_t s);
 
+// Pre-processing: randomized Hadamard rotation and factored scale field.
+constexpr int64_t kHadamardMaxN = 4096;          // longest chunk of the wave kernel
+constexpr int64_t kHadamardSmallMaxLen = 8192;   // row length limit when n < 64
+hipError_t launch_hadamard(const float *X, int64_t ldx, float *Y, int64_t ldy, int64_t rows,
+                           int64_t len, int64_t n, const float *sigma, int inverse,
+                           hipStream_t s);
+size_t scale_field_slabs(int64_t M);
+hipError_t launch_scale_field(const float *W, int64_t ldw, int64_t M, int64_t N, float *a,
+                              float *b, float *Wn, int64_t ldn, float *part, hipStream_t s);
+
 // Error feedback over coding blocks.
 hipError_t launch_ldlq_update(float *tgt, int64_t ldt, const float *W, int64_t ldw,
                               const float *what, int64_t ldh, const float *U, int64_t ldu,
