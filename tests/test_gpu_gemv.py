@@ -3,10 +3,11 @@ followed by a float64 product.
 
 Inputs are seeded random bitstreams with start states below 2^(L-kV) (every such
 stream is a path of the trellis) and N(0,1) activations; nothing comes from the GPU
-encoder.  Bar: the GPU accumulates in fp32 with fmaf, each lane over at most
-ceil(N/64) products, then a tree of at most 8 additions, so for every row
-|y_gpu - y_ref| <= (N/64 + 16) * 2^-24 * sum_i |W_hat[r, i] x_i|  (recursive-summation
-bound, gamma_n <= n u, with margin).
+encoder.  Bar: each row is a sum of N fp32 products formed with fmaf, in some fixed
+order; whatever the order, every term passes through at most N + log2(N) + 8 roundings
+(its own fmaf, the sums it is merged into, the passes over codebook parts), so
+|y_gpu - y_ref| <= 2 (N + 32) 2^-24 sum_i |W_hat[r, i] x_i|  (gamma_m <= m u for m
+roundings, with margin).
 """
 import sys
 
@@ -48,7 +49,7 @@ def _gpu_gemv(bits, s0, C, x, M, N, L, k, V, T):
 
 
 def _check(y, yref, What, x, N):
-    bound = (N / 64 + 16) * 2.0 ** -24 * (np.abs(What.astype(np.float64)) @
+    bound = 2 * (N + 32) * 2.0 ** -24 * (np.abs(What.astype(np.float64)) @
                                           np.abs(x.astype(np.float64))) + 1e-30
     err = np.abs(y.astype(np.float64) - yref)
     bad = np.nonzero(err > bound)[0]
@@ -68,6 +69,8 @@ CASES = [
     (16, 3, 1, 256, 5, 1024),
     (16, 2, 2, 256, 4, 768),
     (16, 1, 1, 17, 3, 17 * 61),
+    (12, 3, 2, 32, 3, 128),
+    (16, 2, 1, 256, 70, 256),
 ]
 
 

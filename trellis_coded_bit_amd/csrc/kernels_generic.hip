@@ -213,44 +213,6 @@ __global__ __launch_bounds__(256) void decode_kernel(
     }
 }
 
-// y = W_hat x with the weights decoded inside the product (Pingala-8 post, decoding
-// paragraph: decode inside the matrix-vector product).  One 256-thread workgroup per
-// row; thread i takes the (block, step) pairs i, i + 256, ... of the row in order and
-// accumulates C[s_t][v] * x with fmaf; the 256 partial sums are added by a fixed tree
-// (wave shuffles, then the 4 waves in order), so results are deterministic.
-__global__ __launch_bounds__(256) void decode_gemv_kernel(
-    const uint32_t *__restrict__ bitstream, const uint32_t *__restrict__ start_state,
-    const float *__restrict__ C, const float *__restrict__ x, float *__restrict__ y,
-    int64_t blocks_per_row, int L, int kv, int V, int n, int nwords) {
-    __shared__ float part[4];
-    const int64_t row = blockIdx.x;
-    const uint32_t tid = threadIdx.x;
-    const uint32_t mask = (1u << L) - 1u;
-    const uint32_t pairs = static_cast<uint32_t>(blocks_per_row) * static_cast<uint32_t>(n);
-    const uint32_t un = static_cast<uint32_t>(n);
-    float acc = 0.0f;
-    for (uint32_t i = tid; i < pairs; i += 256u) {
-        const uint32_t c = i / un;
-        const int t = static_cast<int>(i - c * un) + 1;
-        const int64_t blk = row * blocks_per_row + c;
-        const uint32_t *words = bitstream + blk * nwords;
-        const int P = t * kv;
-        uint32_t s;
-        if (P >= L) {
-            s = stream_bits(words, nwords, P - L, L);
-        } else {
-            s = ((start_state[blk] << P) | stream_bits(words, nwords, 0, P)) & mask;
-        }
-        const float *xc = x + static_cast<int64_t>(i) * V;
-        const float *cs = C + static_cast<int64_t>(s) * V;
-        for (int v = 0; v < V; ++v) acc = __builtin_fmaf(cs[v], xc[v], acc);
-    }
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if ((tid & 63u) == 0) part[tid >> 6] = acc;
-    __syncthreads();
-    if (tid == 0) y[row] = ((part[0] + part[1]) + part[2]) + part[3];
-}
-
 template <bool W, bool LDS>
 hipError_t launch_one(const Problem &p, const Plan &pl, const float *Wm, const float *d,
                       const float *C, int64_t block0, int64_t nb, char *ws, float *cost,
@@ -313,16 +275,6 @@ hipError_t launch_decode(const uint32_t *bitstream, const uint32_t *start_state,
     // grid.x limit is 2^31-1 blocks; the validated sizes stay far below it
     hipLaunchKernelGGL(decode_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(threads), 0, s,
                        bitstream, start_state, C, per_row, L, k * V, V, n, nwords, out, ldo);
-    return hipGetLastError();
-}
-
-hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_state,
-                              const float *C, const float *x, float *y, int64_t M, int64_t N,
-                              int L, int k, int V, int T, hipStream_t s) {
-    const int64_t per_row = N / T;
-    const int nwords = (k * T + 31) / 32;
-    hipLaunchKernelGGL(decode_gemv_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, s,
-                       bitstream, start_state, C, x, y, per_row, L, k * V, V, T / V, nwords);
     return hipGetLastError();
 }
 
