@@ -66,10 +66,15 @@ SMALL = [
 
 
 # L = 16 register-resident kernels: every combination of super-step count parity and
-# leftover steps (k*V = 2: three steps per super-step; k*V = 3: two)
+# leftover steps (k*V = 2: three steps per super-step; k*V = 3: two; k*V = 4: three
+# 2-bit half-steps, i.e. 2n half-steps for n steps)
 L16_EDGES = [(16, 2, 1, n, 2, 2 * n, n % 2 == 0) for n in range(1, 13)] + \
             [(16, 3, 1, n, 2, 2 * n, n % 2 == 1) for n in range(1, 9)] + \
-            [(16, 3, 1, 256, 3, 768, True), (16, 3, 1, 255, 1, 510, False)]
+            [(16, 3, 1, 256, 3, 768, True), (16, 3, 1, 255, 1, 510, False)] + \
+            [(16, 2, 2, 2 * n, 2, 4 * n, n % 2 == 1) for n in range(1, 13)] + \
+            [(16, 4, 1, n, 2, 2 * n, n % 2 == 0) for n in range(1, 9)] + \
+            [(16, 2, 2, 256, 2, 512, True), (16, 2, 2, 254, 1, 508, False),
+             (16, 4, 1, 256, 1, 512, True)]
 
 
 @pytest.mark.parametrize("L,k,V,T,M,N,weighted", SMALL + L16_EDGES)

@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libtcq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["tcq_api.cpp", "codebook.cpp", "kernels_generic.hip", "kernels_l16.hip",
-           "kernels_l16k3.hip", "kernels_ldlq.hip", "kernels_bcjr.hip",
+           "kernels_l16k3.hip", "kernels_l16h.hip", "kernels_ldlq.hip", "kernels_bcjr.hip",
            "kernels_preprocess.hip", "kernels_gemv.hip"]
 
 # -ffp-contract=off: the encoder's fp32 recurrence is written with explicit fmaf and

@@ -1,0 +1,377 @@
+// L = 16, k*V = 4 forward kernel (k = 2, V = 2: the 8B-MLP shape; also k = 4, V = 1).
+//
+// A step that shifts in four bits is two "half-steps" of two bits: the predecessors of
+// s = (x << 4) | b are (j << 12) | x, j = 0..15, and the minimum over j splits into a
+// minimum over the top two bits of j (first half-step, which adds no cost) followed by a
+// minimum over the bottom two (second half-step, which adds the branch metric of the
+// whole step).  The minima are exact, so every cost is the one the 16-way search gives;
+// the bitstream is the same bits read as 2-bit chunks (chunk b_t = (b'_{2t-1} << 2) |
+// b'_{2t}), and the start state s_0 comes out below 2^12 because all costs start equal.
+// Only exact ties between predecessors can be resolved differently from the 16-way
+// search (lowest bottom pair first instead of lowest j), and an exact tie is a runner-up
+// at zero distance.
+//
+// So the kernel is the k*V = 2 kernel (kernels_l16.hip, layout in l16_layout.h) run over
+// 2n half-steps, with the metric only on even half-steps: half-step h = 3q + P of
+// super-step q carries a metric when q + P is even (P = 2 for even q, P = 1 and 3 for
+// odd q).  Metric: for v = 0..V-1 in order, e = fl(w - C[s][v]); acc = fmaf(fl(d e), e,
+// acc), starting from the kept predecessor cost (the encoder's chain).
+#include <hip/hip_runtime.h>
+
+#include <utility>
+
+#include "l16_device.h"
+#include "l16_layout.h"
+#include "tcq.h"
+#include "tcq_internal.h"
+
+namespace tcq {
+namespace {
+
+using namespace l16;
+
+// Codebook copies: for step P (1..3) and coordinate v, per (wave, group, lane) one float4
+// with coordinate v of the group's four successors: 3 V copies of kCopy float4.
+template <int V>
+__global__ __launch_bounds__(256) void l16h_prepare_kernel(const float *__restrict__ C,
+                                                           float4 *__restrict__ out) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= 3 * V * kCopy) return;
+    const int pv = idx / kCopy;
+    const int p = pv / V + 1;
+    const int v = pv % V;
+    const int rem = idx % kCopy;
+    const uint32_t w = rem / (kGroupsPerLane * kLanes);
+    const uint32_t g = (rem / kLanes) % kGroupsPerLane;
+    const uint32_t l = rem % kLanes;
+    const uint32_t s = state_of(p, w, l, group_reg(p, g, 0));  // successors s .. s+3
+    const float *src = C + static_cast<size_t>(s) * V + v;
+    out[idx] = make_float4(src[0], src[V], src[2 * V], src[3 * V]);
+}
+
+// Metric groups of a super-step in processing order.  MP = q mod 2.
+//   MP = 0: step 2 only  -> segments 1, 3          (32 groups)
+//   MP = 1: steps 1 and 3 -> segments 0, 2, 4, 5   (64 groups)
+__host__ __device__ constexpr int metric_groups(int mp) { return mp ? 64 : 32; }
+__host__ __device__ constexpr int metric_seg(int mp, int j) {
+    return mp ? (j == 0 ? 0 : (j == 1 ? 2 : (j == 2 ? 4 : 5))) : (j == 0 ? 1 : 3);
+}
+// does segment SEG of a super-step with pattern MP carry the metric?
+__host__ __device__ constexpr bool seg_has_metric(int mp, int seg) {
+    return ((seg_step(seg) + mp) & 1) == 0;
+}
+// index of segment SEG among the metric segments of pattern MP
+__host__ __device__ constexpr int metric_index(int mp, int seg) {
+    return mp ? (seg == 0 ? 0 : (seg == 2 ? 1 : (seg == 4 ? 2 : 3))) : (seg == 1 ? 0 : 1);
+}
+
+template <int V>
+struct Ring {
+    static constexpr int kSize = 8 * V;  // loads in flight (8 groups)
+};
+
+// Codebook load for metric position K of a super-step with pattern MP (positions run
+// over the metric groups in processing order, V loads per group; positions past the
+// end of the super-step belong to the next one, whose pattern is 1 - MP).
+template <int V, int MP, int K>
+__device__ __forceinline__ float4 cbh_load_pos(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+    constexpr int cnt = metric_groups(MP) * V;
+    constexpr int mp = K < cnt ? MP : 1 - MP;
+    constexpr int k = K < cnt ? K : K - cnt;
+    constexpr int mg = k / V;
+    constexpr int v = k % V;
+    constexpr int seg = metric_seg(mp, mg / 16);
+    constexpr int P = seg_step(seg);
+    constexpr int g = static_cast<int>(seg_group(seg, mg % 16));
+    constexpr int kEntry = static_cast<int>(sizeof(float4));
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(
+        rs, voff + (g & 3) * kLanes * kEntry,
+        (((P - 1) * V + v) * kCopy + (g & ~3) * kLanes) * kEntry, 0);
+    return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                       __uint_as_float(x[3]));
+}
+
+template <int V, int MP, int K0, int... I>
+__device__ __forceinline__ void ringh_prime(float4 (&ring)[Ring<V>::kSize],
+                                            __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                            std::integer_sequence<int, I...>) {
+    ((ring[(K0 + I) % Ring<V>::kSize] = cbh_load_pos<V, MP, K0 + I>(rs, voff)), ...);
+}
+
+// One group (I-th of segment SEG) of a half-step without metric: the four successors all
+// take the kept predecessor cost.
+template <int SEG, int NM, int I>
+__device__ __forceinline__ void acsh_group_plain(uint32_t (&J)[kRegs], uint32_t &acc) {
+    constexpr int P = seg_step(SEG);
+    constexpr uint32_t g = seg_group(SEG, I);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int r0 = phys(NM, group_reg(P, g, 0)), r1 = phys(NM, group_reg(P, g, 1));
+    constexpr int r2 = phys(NM, group_reg(P, g, 2)), r3 = phys(NM, group_reg(P, g, 3));
+    const uint32_t u0 = J[r0], u1 = J[r1], u2 = J[r2], u3 = J[r3];
+    const uint32_t m01 = u0 < u1 ? u0 : u1;
+    const uint32_t m23 = u2 < u3 ? u2 : u3;
+    const uint32_t mu = m01 < m23 ? m01 : m23;
+    const uint64_t c01 = __ballot(u1 < u0);
+    const uint64_t c23 = __ballot(u3 < u2);
+    const uint64_t chi = __ballot(m23 < m01);
+    const uint64_t b0 = (chi & c23) | (~chi & c01);
+    acc = shift_in(shift_in(acc, chi), b0);
+    J[r0] = mu;
+    J[r1] = mu;
+    J[r2] = mu;
+    J[r3] = mu;
+}
+
+// One group of a half-step with metric (V coordinates per successor).
+template <int SEG, bool WEIGHTED, int NM, int V, int MP, int I>
+__device__ __forceinline__ void acsh_group_metric(uint32_t (&J)[kRegs],
+                                                  float4 (&ring)[Ring<V>::kSize],
+                                                  __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                                  const float (&wt)[2], const float (&dt)[2],
+                                                  uint32_t &acc) {
+    constexpr int RS = Ring<V>::kSize;
+    constexpr int P = seg_step(SEG);
+    constexpr int k = (16 * metric_index(MP, SEG) + I) * V;  // first position of the group
+    constexpr uint32_t g = seg_group(SEG, I);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    float4 c[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) c[v] = ring[(k + v) % RS];
+    if constexpr (V == 1) {
+        ring[k % RS] = cbh_load_pos<V, MP, k + RS>(rs, voff);
+    } else {
+        ring[k % RS] = cbh_load_pos<V, MP, k + RS>(rs, voff);
+        ring[(k + 1) % RS] = cbh_load_pos<V, MP, k + 1 + RS>(rs, voff);
+    }
+    constexpr int r0 = phys(NM, group_reg(P, g, 0)), r1 = phys(NM, group_reg(P, g, 1));
+    constexpr int r2 = phys(NM, group_reg(P, g, 2)), r3 = phys(NM, group_reg(P, g, 3));
+    const uint32_t u0 = J[r0], u1 = J[r1], u2 = J[r2], u3 = J[r3];
+    const uint32_t m01 = u0 < u1 ? u0 : u1;
+    const uint32_t m23 = u2 < u3 ? u2 : u3;
+    const uint32_t mu = m01 < m23 ? m01 : m23;
+    const uint64_t c01 = __ballot(u1 < u0);
+    const uint64_t c23 = __ballot(u3 < u2);
+    const uint64_t chi = __ballot(m23 < m01);
+    const uint64_t b0 = (chi & c23) | (~chi & c01);
+    acc = shift_in(shift_in(acc, chi), b0);
+    float a0 = __uint_as_float(mu), a1 = a0, a2 = a0, a3 = a0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const float e0 = wt[v] - c[v].x, e1 = wt[v] - c[v].y;
+        const float e2 = wt[v] - c[v].z, e3 = wt[v] - c[v].w;
+        a0 = __builtin_fmaf(WEIGHTED ? dt[v] * e0 : e0, e0, a0);
+        a1 = __builtin_fmaf(WEIGHTED ? dt[v] * e1 : e1, e1, a1);
+        a2 = __builtin_fmaf(WEIGHTED ? dt[v] * e2 : e2, e2, a2);
+        a3 = __builtin_fmaf(WEIGHTED ? dt[v] * e3 : e3, e3, a3);
+    }
+    J[r0] = __float_as_uint(a0);
+    J[r1] = __float_as_uint(a1);
+    J[r2] = __float_as_uint(a2);
+    J[r3] = __float_as_uint(a3);
+}
+
+template <int SEG, bool WEIGHTED, int NM, int V, int MP, int... I>
+__device__ __forceinline__ void acsh_segment_impl(uint32_t (&J)[kRegs],
+                                                  float4 (&ring)[Ring<V>::kSize],
+                                                  const Ctx &cx, const float (&wt)[2],
+                                                  const float (&dt)[2], uint32_t *bp_word,
+                                                  std::integer_sequence<int, I...>) {
+    uint32_t acc = 0;
+    if constexpr (seg_has_metric(MP, SEG)) {
+        (acsh_group_metric<SEG, WEIGHTED, NM, V, MP, I>(J, ring, cx.rs, cx.voff, wt, dt, acc),
+         ...);
+    } else {
+        (acsh_group_plain<SEG, NM, I>(J, acc), ...);
+    }
+    *bp_word = acc;
+}
+
+// Segment SEG of super-step q (half-steps 3q + 1 .. 3q + 3), pattern MP = q mod 2.
+template <int SEG, bool WEIGHTED, int NM, int V, int MP>
+__device__ __forceinline__ void acsh_segment(uint32_t (&J)[kRegs],
+                                             float4 (&ring)[Ring<V>::kSize], const Ctx &cx,
+                                             int h0) {
+    constexpr int P = seg_step(SEG);
+    const int h = h0 + P - 1;  // 0-based half-step index
+    float wt[2] = {0.0f, 0.0f}, dt[2] = {1.0f, 1.0f};
+    if constexpr (seg_has_metric(MP, SEG)) {
+        const int t = h >> 1;  // 0-based full step (h is odd here)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            wt[v] = cx.wcol[t * V + v];
+            if (WEIGHTED) dt[v] = cx.dcol[t * V + v];
+        }
+    }
+    acsh_segment_impl<SEG, WEIGHTED, NM, V, MP>(J, ring, cx, wt, dt,
+                                                cx.bp + 2 * kThreads * h + seg_half(SEG),
+                                                std::make_integer_sequence<int, 16>{});
+}
+
+// Super-step under naming NM and pattern MP; entry and exit as in kernels_l16.hip.
+template <bool WEIGHTED, int NM, int V, int MP>
+__device__ __forceinline__ void super_step_h(uint32_t (&J)[kRegs],
+                                             float4 (&ring)[Ring<V>::kSize], const Ctx &cx,
+                                             int h0) {
+    acsh_segment<0, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
+    acsh_segment<1, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
+    __syncthreads();  // round-1 values written by every wave
+    round_read<1 - NM, 1>(J, cx);
+    acsh_segment<2, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
+    acsh_segment<3, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
+    acsh_segment<4, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
+    __syncthreads();  // every wave has read round 1
+    round_write<NM, 0>(J, cx);
+    acsh_segment<5, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
+    __syncthreads();  // round-0 values written by every wave
+    round_read<NM, 0>(J, cx);
+    __syncthreads();  // every wave has read round 0
+    round_write<NM, 1>(J, cx);
+}
+
+// The last R = 1 or 2 half-steps (segments 0..3 in order) under naming 0.  The metric
+// positions they use are the first ones of their pattern, in order, so the ring needs
+// no refill.
+template <bool WEIGHTED, int V, int MP, int R>
+__device__ __forceinline__ void tail_h(uint32_t (&J)[kRegs], float4 (&ring)[Ring<V>::kSize],
+                                       const Ctx &cx, int h0) {
+    acsh_segment<0, WEIGHTED, 0, V, MP>(J, ring, cx, h0);
+    if constexpr (R == 2) acsh_segment<1, WEIGHTED, 0, V, MP>(J, ring, cx, h0);
+    __syncthreads();
+    round_read<1, 1>(J, cx);
+    acsh_segment<2, WEIGHTED, 0, V, MP>(J, ring, cx, h0);
+    if constexpr (R == 2) acsh_segment<3, WEIGHTED, 0, V, MP>(J, ring, cx, h0);
+}
+
+template <int P, int NM>
+__device__ __forceinline__ void lane_argmin_h(const uint32_t (&J)[kRegs], uint32_t w,
+                                              uint32_t l, uint32_t &bv, uint32_t &bi) {
+    const uint32_t lanepart = state_of(P, w, l, 0);
+#pragma unroll
+    for (int r = 0; r < kRegs; ++r) {
+        const uint32_t s = lanepart | state_of(P, 0, 0, r);
+        const uint32_t v = J[phys(NM, r)];
+        if (v < bv || (v == bv && s < bi)) {
+            bv = v;
+            bi = s;
+        }
+    }
+}
+
+// n = full steps per block; the kernel runs 2n half-steps.
+template <bool WEIGHTED, int V>
+__global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
+    const float *__restrict__ W, int64_t ldw, const float *__restrict__ d,
+    const float4 *__restrict__ cb, int n, int64_t blocks_per_row, int64_t block0,
+    uint2 *__restrict__ bp, int64_t bp_per_block, uint32_t *__restrict__ send,
+    float *__restrict__ cost_out) {
+    const uint32_t tid = threadIdx.x;
+    const uint32_t w = tid >> 6;
+    const uint32_t l = tid & 63;
+    const int64_t blk = block0 + blockIdx.x;
+    const int64_t row = blk / blocks_per_row;
+    const int64_t col = blk % blocks_per_row;
+    const Ctx cx = make_ctx(W, ldw, WEIGHTED ? d : nullptr, cb, n * V, row, col, w, l,
+                            bp + blockIdx.x * bp_per_block, 3 * V);
+
+    uint32_t J[kRegs];
+#pragma unroll
+    for (int r = 0; r < kRegs; ++r) J[r] = 0u;
+#pragma unroll
+    for (int r = 0; r < kRegs; ++r) asm volatile("" : "+v"(J[r]));
+    constexpr int RS = Ring<V>::kSize;
+    float4 ring[RS];
+    ringh_prime<V, 0, 0>(ring, cx.rs, cx.voff, std::make_integer_sequence<int, RS>{});
+    round_write<1, 1>(J, cx);
+
+    const int nh = 2 * n;
+    const int Q = nh / 3;
+    const int R = nh % 3;
+    if (Q & 1) {
+        super_step_h<WEIGHTED, 1, V, 0>(J, ring, cx, 0);
+        for (int q = 1; q < Q; q += 2) {
+            super_step_h<WEIGHTED, 0, V, 1>(J, ring, cx, 3 * q);
+            super_step_h<WEIGHTED, 1, V, 0>(J, ring, cx, 3 * q + 3);
+        }
+    } else {
+        for (int q = 0; q < Q; q += 2) {
+            super_step_h<WEIGHTED, 0, V, 0>(J, ring, cx, 3 * q);
+            super_step_h<WEIGHTED, 1, V, 1>(J, ring, cx, 3 * q + 3);
+        }
+    }
+    // the tail is super-step Q, pattern Q mod 2
+    if (R == 1) {
+        if (Q & 1) tail_h<WEIGHTED, V, 1, 1>(J, ring, cx, 3 * Q);
+        else tail_h<WEIGHTED, V, 0, 1>(J, ring, cx, 3 * Q);
+    } else if (R == 2) {
+        if (Q & 1) tail_h<WEIGHTED, V, 1, 2>(J, ring, cx, 3 * Q);
+        else tail_h<WEIGHTED, V, 0, 2>(J, ring, cx, 3 * Q);
+    } else {
+        __syncthreads();
+        round_read<1, 1>(J, cx);
+    }
+
+    uint32_t bv = 0xFFFFFFFFu;
+    uint32_t bi = 0xFFFFFFFFu;
+    if (R == 1) lane_argmin_h<1, 0>(J, w, l, bv, bi);
+    else if (R == 2) lane_argmin_h<2, 0>(J, w, l, bv, bi);
+    else lane_argmin_h<0, 0>(J, w, l, bv, bi);
+    block_select(bv, bi, w, l, send + blockIdx.x, cost_out + blk);
+}
+
+constexpr size_t kLdsBytes = kLdsDwords * sizeof(float);
+
+template <bool WEIGHTED, int V>
+hipError_t launch_h(const Problem &p, int64_t block0, int64_t nb, const float *W,
+                    const float *d, const float4 *cb, uint2 *bp, int64_t bp_per_block,
+                    uint32_t *send, float *cost, hipStream_t s) {
+    auto kern = acs_l16h_kernel<WEIGHTED, V>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(kLdsBytes));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nb)), dim3(kThreads), kLdsBytes, s, W,
+                       p.ldw, d, cb, p.n, p.blocks_per_row, block0, bp, bp_per_block, send,
+                       cost);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool l16h_supported(const Problem &p) {
+    return p.L == 16 && p.kv == 4 && (p.V == 1 || p.V == 2);
+}
+
+size_t l16h_fixed_bytes(const Problem &p) { return 3 * p.V * sizeof(float4) * kCopy; }
+
+// two words per lane and half-step, 2n half-steps
+size_t l16h_bp_bytes(const Problem &p) {
+    return static_cast<size_t>(2 * p.n) * kThreads * sizeof(uint2);
+}
+
+hipError_t launch_l16h_prepare(const Problem &p, const float *C, char *ws, hipStream_t s) {
+    const int total = 3 * p.V * kCopy;
+    if (p.V == 2)
+        hipLaunchKernelGGL(l16h_prepare_kernel<2>, dim3((total + 255) / 256), dim3(256), 0, s, C,
+                           reinterpret_cast<float4 *>(ws));
+    else
+        hipLaunchKernelGGL(l16h_prepare_kernel<1>, dim3((total + 255) / 256), dim3(256), 0, s, C,
+                           reinterpret_cast<float4 *>(ws));
+    return hipGetLastError();
+}
+
+hipError_t launch_acs_l16h(const Problem &p, const Plan &pl, const float *W, const float *d,
+                           int64_t block0, int64_t nb, char *ws, float *cost, hipStream_t s) {
+    char *per = ws + pl.fixed;
+    uint2 *bp = reinterpret_cast<uint2 *>(per);
+    uint32_t *send = reinterpret_cast<uint32_t *>(per + nb * pl.bp_bytes);
+    const float4 *cb = reinterpret_cast<const float4 *>(ws);
+    const int64_t bpb = static_cast<int64_t>(pl.bp_bytes / sizeof(uint2));
+    if (p.V == 2)
+        return d ? launch_h<true, 2>(p, block0, nb, W, d, cb, bp, bpb, send, cost, s)
+                 : launch_h<false, 2>(p, block0, nb, W, d, cb, bp, bpb, send, cost, s);
+    return d ? launch_h<true, 1>(p, block0, nb, W, d, cb, bp, bpb, send, cost, s)
+             : launch_h<false, 1>(p, block0, nb, W, d, cb, bp, bpb, send, cost, s);
+}
+
+}  // namespace tcq

@@ -34,19 +34,21 @@ struct Ctx {
     uint32_t rb[4];             // LDS byte bases for round reads
 };
 
-// Context of one coding block (row, col) for lane l of wave w.  The codebook copies
-// start at cb; each wave addresses its own 2048-entry slice of every copy through a
-// raw buffer descriptor, so every load is (16 * lane) + scalar offset + immediate.
+// Context of one coding block (row, col) for lane l of wave w; n is the block length in
+// weights.  The `copies` codebook copies start at cb; each wave addresses its own
+// 2048-entry slice of every copy through a raw buffer descriptor, so every load is
+// (16 * lane) + scalar offset + immediate.
 __device__ __forceinline__ Ctx make_ctx(const float *W, int64_t ldw, const float *d,
                                         const float4 *cb, int n, int64_t row, int64_t col,
-                                        uint32_t w, uint32_t l, uint2 *bp_block) {
+                                        uint32_t w, uint32_t l, uint2 *bp_block,
+                                        int copies = 3) {
     Ctx cx;
     const uint32_t wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform
     cx.wcol = W + row * ldw + col * n;
     cx.dcol = d ? d + col * n : nullptr;
     // CDNA buffer descriptor word 3 (raw dword access), as used for gfx9-family parts
     cx.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float4 *>(cb + wu * (kCopy / kWaves)),
-                                              0, 3 * kCopy * static_cast<int>(sizeof(float4)),
+                                              0, copies * kCopy * static_cast<int>(sizeof(float4)),
                                               0x00020000);
     cx.voff = l * static_cast<uint32_t>(sizeof(float4));
     cx.bp = reinterpret_cast<uint32_t *>(bp_block + (w * kLanes + l));

@@ -41,6 +41,11 @@ Plan plan_for(const Problem &p) {
         pl.fixed = align_up(l16k3_fixed_bytes(p), 256);
         pl.bp_bytes = align_up(l16k3_bp_bytes(p), 256);
         pl.cost_bytes = 0;
+    } else if (l16h_supported(p)) {
+        pl.variant = kL16RegsHalf;
+        pl.fixed = align_up(l16h_fixed_bytes(p), 256);
+        pl.bp_bytes = align_up(l16h_bp_bytes(p), 256);
+        pl.cost_bytes = 0;
     } else {
         const int64_t nw64 = (p.ngroups + 63) / 64;
         pl.bp_bytes = align_up(static_cast<size_t>(p.n) * p.kv * nw64 * 8, 256);
@@ -195,6 +200,9 @@ static int encode_impl(const char *fn, const float *W, int64_t M, int64_t N, int
     } else if (pl.variant == kL16RegsK3) {
         e = launch_l16k3_prepare(p, codebook, ws, stream);
         if (e != hipSuccess) return hip_fail(fn, "codebook preparation launch", e);
+    } else if (pl.variant == kL16RegsHalf) {
+        e = launch_l16h_prepare(p, codebook, ws, stream);
+        if (e != hipSuccess) return hip_fail(fn, "codebook preparation launch", e);
     }
     for (int64_t b0 = 0; b0 < p.nblocks; b0 += batch) {
         const int64_t nb = (p.nblocks - b0 < batch) ? p.nblocks - b0 : batch;
@@ -210,6 +218,22 @@ static int encode_impl(const char *fn, const float *W, int64_t M, int64_t N, int
                 if (e != hipSuccess) return hip_fail(fn, "hipEventRecord", e);
             }
             e = launch_traceback_l16(p, pl, b0, nb, ws, bitstream, start_state, stream);
+            if (e != hipSuccess) return hip_fail(fn, "traceback launch", e);
+        } else if (pl.variant == kL16RegsHalf) {
+            e = launch_acs_l16h(p, pl, W, d, b0, nb, ws, cost, stream);
+            if (e != hipSuccess) return hip_fail(fn, "ACS launch", e);
+            if (b0 + nb >= p.nblocks && acs_end) {
+                e = hipEventRecord(acs_end, stream);
+                if (e != hipSuccess) return hip_fail(fn, "hipEventRecord", e);
+            }
+            // the 2-bit half-step view: 2n steps of k = 2, V = 1 give the same bits
+            Problem ph = p;
+            ph.k = 2;
+            ph.V = 1;
+            ph.kv = 2;
+            ph.n = 2 * p.n;
+            ph.T = 2 * p.n;
+            e = launch_traceback_l16(ph, pl, b0, nb, ws, bitstream, start_state, stream);
             if (e != hipSuccess) return hip_fail(fn, "traceback launch", e);
         } else if (pl.variant == kL16RegsK3) {
             e = launch_acs_l16k3(p, pl, W, d, b0, nb, ws, cost, stream);

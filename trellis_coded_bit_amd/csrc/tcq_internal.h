@@ -35,6 +35,7 @@ enum Variant : int {
     kGenericGlobal = 1,  // any supported shape, cost vectors in the workspace (L2)
     kL16Regs = 2,        // L = 16, k*V = 2, costs in VGPRs (three-step super-steps)
     kL16RegsK3 = 3,      // L = 16, k*V = 3, costs in VGPRs (two-step super-steps)
+    kL16RegsHalf = 4,    // L = 16, k*V = 4 (V = 1, 2), run as 2-bit half-steps in VGPRs
 };
 
 Plan plan_for(const Problem &p);
@@ -95,6 +96,14 @@ hipError_t launch_acs_l16(const Problem &p, const Plan &pl, const float *W, cons
 hipError_t launch_traceback_l16(const Problem &p, const Plan &pl, int64_t block0, int64_t nb,
                                 const char *ws, uint32_t *bitstream, uint32_t *start_state,
                                 hipStream_t s);
+
+// L = 16, k*V = 4 register-resident path (half-steps).
+bool l16h_supported(const Problem &p);
+size_t l16h_fixed_bytes(const Problem &p);
+size_t l16h_bp_bytes(const Problem &p);
+hipError_t launch_l16h_prepare(const Problem &p, const float *C, char *fixed_ws, hipStream_t s);
+hipError_t launch_acs_l16h(const Problem &p, const Plan &pl, const float *W, const float *d,
+                           int64_t block0, int64_t nb, char *ws, float *cost, hipStream_t s);
 
 // L = 16, k*V = 3 register-resident path.
 bool l16k3_supported(const Problem &p);
