@@ -101,11 +101,19 @@ def cpu_baseline(w, W, d, C, nblocks, threads):
     t0 = time.perf_counter()
     oracle.encode_matrix(W, d, C, w.L, w.k, w.V, w.T, blocks=blocks, threads=threads)
     dt = time.perf_counter() - t0
+    # one core: the first 32 of those blocks on a single thread
+    one = blocks[:32]
+    t1 = time.perf_counter()
+    oracle.encode_matrix(W, d, C, w.L, w.k, w.V, w.T, blocks=one, threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": blocks.size * w.T / dt, "unit": "weights/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{blocks.size} seeded-random blocks of the same workload "
                       f"({blocks.size * w.T} weights), one block per thread at a time, "
-                      f"{dt:.2f} s wall"}
+                      f"{dt:.2f} s wall",
+            "value_1core": one.size * w.T / dt1,
+            "sample_1core": f"the first {one.size} of those blocks on one thread, "
+                            f"{dt1:.2f} s"}
 
 
 def gemv_bench(torch, _lib, w, enc, Ct, iters):

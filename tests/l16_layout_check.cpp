@@ -8,7 +8,9 @@
 //    the same state at p = 0;
 //  - LDS staging addresses are in range, distinct within a round, agree between the
 //    writing and the reading side, and every wave instruction touches distinct banks
-//    (64 banks per wave, 32 per half wave).
+//    (64 banks per wave, 32 per half wave);
+//  - the k*V = 4 half-step patterns place the metric on the even half-steps and list
+//    every metric group once, in processing order.
 #define __host__
 #define __device__
 #include <cstdio>
@@ -194,6 +196,28 @@ int main() {
             }
         }
         CHECK(gs.size() == 16 && slots.size() == 16);
+    }
+    // k*V = 4 half-steps: the metric positions of each pattern cover every metric group
+    // once, in processing order, and the pattern follows the half-step parity
+    for (int mp = 0; mp <= 1; ++mp) {
+        std::set<uint32_t> seen;
+        int expect = 0;
+        for (int seg = 0; seg < 6; ++seg) {
+            CHECK(seg_has_metric(mp, seg) == (((seg_step(seg) + mp) % 2) == 0));
+            if (!seg_has_metric(mp, seg)) continue;
+            CHECK(metric_index(mp, seg) == expect);
+            CHECK(metric_seg(mp, expect) == seg);
+            for (int i = 0; i < 16; ++i)
+                seen.insert(static_cast<uint32_t>(seg_step(seg)) * 64u + seg_group(seg, i));
+            ++expect;
+        }
+        CHECK(expect * 16 == metric_groups(mp));
+        CHECK((int)seen.size() == metric_groups(mp));
+        for (int q = mp; q < mp + 8; q += 2)
+            for (int seg = 0; seg < 6; ++seg)
+                CHECK(seg_has_metric(q & 1, seg) == ((3 * q + seg_step(seg)) % 2 == 0));
+        // ring sizes 8 V divide the positions of every super-step
+        for (int V = 1; V <= 2; ++V) CHECK((metric_groups(mp) * V) % (8 * V) == 0);
     }
     if (fails) {
         std::printf("%d failures\n", fails);

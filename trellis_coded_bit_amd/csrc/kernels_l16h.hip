@@ -49,22 +49,6 @@ __global__ __launch_bounds__(256) void l16h_prepare_kernel(const float *__restri
     out[idx] = make_float4(src[0], src[V], src[2 * V], src[3 * V]);
 }
 
-// Metric groups of a super-step in processing order.  MP = q mod 2.
-//   MP = 0: step 2 only  -> segments 1, 3          (32 groups)
-//   MP = 1: steps 1 and 3 -> segments 0, 2, 4, 5   (64 groups)
-__host__ __device__ constexpr int metric_groups(int mp) { return mp ? 64 : 32; }
-__host__ __device__ constexpr int metric_seg(int mp, int j) {
-    return mp ? (j == 0 ? 0 : (j == 1 ? 2 : (j == 2 ? 4 : 5))) : (j == 0 ? 1 : 3);
-}
-// does segment SEG of a super-step with pattern MP carry the metric?
-__host__ __device__ constexpr bool seg_has_metric(int mp, int seg) {
-    return ((seg_step(seg) + mp) & 1) == 0;
-}
-// index of segment SEG among the metric segments of pattern MP
-__host__ __device__ constexpr int metric_index(int mp, int seg) {
-    return mp ? (seg == 0 ? 0 : (seg == 2 ? 1 : (seg == 4 ? 2 : 3))) : (seg == 1 ? 0 : 1);
-}
-
 template <int V>
 struct Ring {
     static constexpr int kSize = 8 * V;  // loads in flight (8 groups)

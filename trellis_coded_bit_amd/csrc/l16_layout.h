@@ -165,6 +165,28 @@ __host__ __device__ constexpr uint32_t bp_shift(int p, uint32_t g) {
     return 2u * (15u - (p == 3 ? (g & 15u) : (g >> 1)));
 }
 
+// ---------------------------------------------------------------------------------
+// k*V = 4 run as 2-bit half-steps (kernels_l16h.hip): super-step q covers half-steps
+// 3q + 1 .. 3q + 3 and the metric sits on the even ones, i.e. on step P of the
+// super-step when q + P is even.  MP = q mod 2 is the super-step's pattern.
+// ---------------------------------------------------------------------------------
+// Metric groups of a super-step in processing order.  MP = q mod 2.
+//   MP = 0: step 2 only  -> segments 1, 3          (32 groups)
+//   MP = 1: steps 1 and 3 -> segments 0, 2, 4, 5   (64 groups)
+__host__ __device__ constexpr int metric_groups(int mp) { return mp ? 64 : 32; }
+__host__ __device__ constexpr int metric_seg(int mp, int j) {
+    return mp ? (j == 0 ? 0 : (j == 1 ? 2 : (j == 2 ? 4 : 5))) : (j == 0 ? 1 : 3);
+}
+// does segment SEG of a super-step with pattern MP carry the metric?
+__host__ __device__ constexpr bool seg_has_metric(int mp, int seg) {
+    return ((seg_step(seg) + mp) & 1) == 0;
+}
+// index of segment SEG among the metric segments of pattern MP
+__host__ __device__ constexpr int metric_index(int mp, int seg) {
+    return mp ? (seg == 0 ? 0 : (seg == 2 ? 1 : (seg == 4 ? 2 : 3))) : (seg == 1 ? 0 : 1);
+}
+
+
 // Register naming.  Odd super-steps keep logical register r in physical register
 // phys(1, r) = r with bits 0 and 6 swapped.  A transposition round then refills exactly
 // the physical registers it has just written out: round 0 moves logical r[6] = 0 into
