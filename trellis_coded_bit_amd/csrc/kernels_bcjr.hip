@@ -281,6 +281,259 @@ __global__ __launch_bounds__(max_threads(KV)) void bcjr_kernel(BcjrArgs a) {
     }
 }
 
+// Register-codebook variant for V = 1 (L - 2 kv >= log2(NT)).  Thread tid owns the y
+// values y_i = tid + NT i (i < NY), and with them the states
+//     s = (j << (L - kv)) | (y << kv) | b,   j, b < 2^kv.
+// In the forward pass these are the predecessors of its groups x = (y << kv) | b; in the
+// backward pass they are the successors of its groups x' = (j << (L - 2 kv)) | y.  So the
+// thread's codebook values never change and stay in registers for the whole block, and
+// the G forward values F(s >> kv) (or backward values B(s mod 2^(L-kv))) that a y needs
+// are read from LDS once and shared by its G groups.  LDS vectors are padded by one
+// float every 32 to spread the strided accesses over the banks.
+__device__ __forceinline__ int pad(int64_t i) { return static_cast<int>(i + (i >> 5)); }
+// y values per thread that fit in registers (NY G^2 codebook floats)
+constexpr int reg_max_ny(int kv) { return kv == 2 ? 8 : 2; }
+
+template <int KV, int NT>
+__global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
+    extern __shared__ float lds[];
+    __shared__ float part_max[2][kMaxWaves];
+    __shared__ float part_m[kMaxWaves], part_s[kMaxWaves];
+    __shared__ float part_u[2][kMaxWaves];
+    __shared__ float part_num[2][kMaxWaves];
+    __shared__ float part_den[2][kMaxWaves];
+
+    constexpr int G = 1 << KV;
+    constexpr int nwaves = NT / 64;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int L = a.L;
+    const int n = a.n;
+    const int64_t X = int64_t{1} << (L - KV);
+    const int shF = L - KV;      // j position in a state
+    const int shY = L - 2 * KV;  // j position in a backward group
+    const int NY = static_cast<int>((int64_t{1} << shY) / NT);
+    const int64_t blk = a.block0 + blockIdx.x;
+    const int64_t row = blk / a.blocks_per_row;
+    const int64_t col = blk % a.blocks_per_row;
+    const float *w = a.W + row * a.ldw + col * n;
+    const float *dd = a.d ? a.d + col * n : nullptr;
+    const bool weighted = a.d != nullptr;
+    float *fst = a.fstore + static_cast<int64_t>(blockIdx.x) * a.fstore_per_block;
+    const int64_t padded = X + (X >> 5);
+    float *bufA = lds;
+    float *bufB = lds + padded;
+    const float ns = a.ns;
+
+    constexpr int kMaxNY = reg_max_ny(KV);
+    float creg[kMaxNY][G][G];
+#pragma unroll
+    for (int iy = 0; iy < kMaxNY; ++iy) {
+        if (iy < NY) {
+            const int64_t y = tid + static_cast<int64_t>(NT) * iy;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float *src = a.C + ((static_cast<int64_t>(j) << shF) | (y << KV));
+#pragma unroll
+                for (int b = 0; b < G; ++b) creg[iy][j][b] = src[b];
+            }
+        }
+    }
+    for (int64_t x = tid; x < X; x += NT) {
+        bufA[pad(x)] = 0.0f;
+        fst[x] = 0.0f;  // F_0
+    }
+    __syncthreads();
+
+    // ---------------- forward ----------------
+    float *Fc = bufA;
+    float *Fn = bufB;
+    double offset = 0.0;
+    for (int t = 1; t <= n; ++t) {
+        float c = 0.0f;
+        if (t >= 2) {
+            c = part_max[(t - 1) & 1][0];
+            for (int i = 1; i < nwaves; ++i) c = fmaxf(c, part_max[(t - 1) & 1][i]);
+            offset += static_cast<double>(c);
+        }
+        const float wt = w[t - 1];
+        const float dt = weighted ? dd[t - 1] : 1.0f;
+        float lmax = kNegInf;
+#pragma unroll
+        for (int iy = 0; iy < kMaxNY; ++iy) {
+            if (iy >= NY) break;
+            const int64_t y = tid + static_cast<int64_t>(NT) * iy;
+            float fj[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) fj[j] = Fc[pad((static_cast<int64_t>(j) << shY) | y)];
+            float fo[G];
+#pragma unroll
+            for (int b = 0; b < G; ++b) {
+                float val[G];
+                float mx = kNegInf;
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    const float e = wt - creg[iy][j][b];
+                    const float m = __builtin_fmaf(weighted ? dt * e : e, e, 0.0f);
+                    val[j] = m * ns + fj[j];
+                    mx = fmaxf(mx, val[j]);
+                }
+                float sum = 0.0f;
+#pragma unroll
+                for (int j = 0; j < G; ++j) sum += exp2_(val[j] - mx);
+                fo[b] = mx + log2_(sum) - c;
+                lmax = fmaxf(lmax, fo[b]);
+            }
+            const int64_t x0 = y << KV;
+#pragma unroll
+            for (int b = 0; b < G; ++b) Fn[pad(x0 + b)] = fo[b];
+            if (t < n) {
+#pragma unroll
+                for (int b = 0; b < G; ++b) fst[static_cast<int64_t>(t) * X + x0 + b] = fo[b];
+            }
+        }
+        lmax = wave_max(lmax);
+        if (lane == 0) part_max[t & 1][wave] = lmax;
+        __syncthreads();
+        float *tmp = Fc;
+        Fc = Fn;
+        Fn = tmp;
+    }
+    {
+        float m = kNegInf, s2 = 0.0f;
+        for (int64_t x = tid; x < X; x += NT) lse_merge(m, s2, Fc[pad(x)], 1.0f);
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float om = __shfl_xor(m, off);
+            const float os = __shfl_xor(s2, off);
+            lse_merge(m, s2, om, os);
+        }
+        if (lane == 0) {
+            part_m[wave] = m;
+            part_s[wave] = s2;
+        }
+        __syncthreads();
+        if (tid == 0 && a.logz) {
+            float fm = part_m[0], fs = part_s[0];
+            for (int i = 1; i < nwaves; ++i) lse_merge(fm, fs, part_m[i], part_s[i]);
+            const double l2 = static_cast<double>(fm) + static_cast<double>(log2_(fs)) + offset;
+            a.logz[blk] = static_cast<float>(l2 * 0.69314718055994530942);
+        }
+    }
+    __threadfence();
+    __syncthreads();
+
+    // ---------------- backward ----------------
+    float *Bc = bufA;
+    float *Bn = bufB;
+    for (int64_t x = tid; x < X; x += NT) Bc[pad(x)] = 0.0f;
+    __syncthreads();
+    float *out = a.soft + row * a.ldo + col * n;
+    for (int t = n; t >= 1; --t) {
+        float c = 0.0f;
+        if (t < n) {
+            c = part_max[(t + 1) & 1][0];
+            for (int i = 1; i < nwaves; ++i) c = fmaxf(c, part_max[(t + 1) & 1][i]);
+        }
+        const float wt = w[t - 1];
+        const float dt = weighted ? dd[t - 1] : 1.0f;
+        float eu = kNegInf, enum_ = 0.0f, eden = 0.0f;
+        float lmax = kNegInf;
+#pragma unroll
+        for (int iy = 0; iy < kMaxNY; ++iy) {
+            if (iy >= NY) break;
+            const int64_t y = tid + static_cast<int64_t>(NT) * iy;
+            float bb[G];
+#pragma unroll
+            for (int b = 0; b < G; ++b) bb[b] = Bc[pad((y << KV) | b)];
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int64_t xg = (static_cast<int64_t>(j) << shY) | y;
+                const float fx = fst[static_cast<int64_t>(t - 1) * X + xg];
+                float val[G];
+                float mx = kNegInf;
+#pragma unroll
+                for (int b = 0; b < G; ++b) {
+                    const float e = wt - creg[iy][j][b];
+                    const float m = __builtin_fmaf(weighted ? dt * e : e, e, 0.0f);
+                    val[b] = m * ns + bb[b];
+                    mx = fmaxf(mx, val[b]);
+                }
+                float sum = 0.0f, gnum = 0.0f;
+#pragma unroll
+                for (int b = 0; b < G; ++b) {
+                    const float e = exp2_(val[b] - mx);
+                    sum += e;
+                    gnum = __builtin_fmaf(e, creg[iy][j][b], gnum);
+                }
+                if (t > 1) {
+                    const float bnew = mx + log2_(sum) - c;
+                    Bn[pad(xg)] = bnew;
+                    lmax = fmaxf(lmax, bnew);
+                }
+                const float gu = mx + fx;
+                const float nm = fmaxf(eu, gu);
+                const float sa = (eu == kNegInf) ? 0.0f : exp2_(eu - nm);
+                const float sb = exp2_(gu - nm);
+                enum_ = enum_ * sa + gnum * sb;
+                eden = eden * sa + sum * sb;
+                eu = nm;
+            }
+        }
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ou = __shfl_xor(eu, off);
+            const float onum = __shfl_xor(enum_, off);
+            const float oden = __shfl_xor(eden, off);
+            const float nm = fmaxf(eu, ou);
+            if (nm != kNegInf) {
+                const float sa = (eu == kNegInf) ? 0.0f : exp2_(eu - nm);
+                const float sb = (ou == kNegInf) ? 0.0f : exp2_(ou - nm);
+                enum_ = enum_ * sa + onum * sb;
+                eden = eden * sa + oden * sb;
+                eu = nm;
+            }
+        }
+        lmax = wave_max(lmax);
+        if (lane == 0) {
+            part_max[t & 1][wave] = lmax;
+            part_u[t & 1][wave] = eu;
+            part_num[t & 1][wave] = enum_;
+            part_den[t & 1][wave] = eden;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float tu = part_u[t & 1][0], tn = part_num[t & 1][0], td = part_den[t & 1][0];
+            for (int i = 1; i < nwaves; ++i) {
+                const float ou = part_u[t & 1][i];
+                const float nm = fmaxf(tu, ou);
+                if (nm == kNegInf) continue;
+                const float sa = (tu == kNegInf) ? 0.0f : exp2_(tu - nm);
+                const float sb = (ou == kNegInf) ? 0.0f : exp2_(ou - nm);
+                tn = tn * sa + part_num[t & 1][i] * sb;
+                td = td * sa + part_den[t & 1][i] * sb;
+                tu = nm;
+            }
+            out[t - 1] = tn / td;
+        }
+        float *tmp = Bc;
+        Bc = Bn;
+        Bn = tmp;
+    }
+}
+
+template <int KV, int NT>
+hipError_t launch_reg(const BcjrArgs &a, int64_t nb, hipStream_t s) {
+    const int64_t X = int64_t{1} << (a.L - KV);
+    const size_t shmem = 2 * static_cast<size_t>(X + (X >> 5)) * sizeof(float);
+    auto kern = bcjr_reg_kernel<KV, NT>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(shmem));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nb)), dim3(NT), shmem, s, a);
+    return hipGetLastError();
+}
+
 template <int KV, bool IN_LDS>
 hipError_t launch_kv(const BcjrArgs &a, int64_t nb, int threads, size_t shmem, hipStream_t s) {
     auto kern = bcjr_kernel<KV, IN_LDS>;
@@ -349,6 +602,15 @@ hipError_t launch_bcjr(const float *W, int64_t ldw, const float *d, const float 
     a.soft = soft;
     a.ldo = ldo;
     a.logz = logz;
+    // register-codebook kernel: V = 1, 2^(L - 2 kv) a multiple of the workgroup size,
+    // at most 4 y values per thread, vectors in LDS
+    if (V == 1 && in_lds && (kv == 2 || kv == 3)) {
+        const int nt = 512;
+        const int64_t ys = int64_t{1} << (L - 2 * kv);
+        const size_t need = 2 * static_cast<size_t>(X + (X >> 5)) * sizeof(float);
+        if (ys % nt == 0 && ys / nt <= reg_max_ny(kv) && need <= kBcjrLdsBytes + (8u << 10))
+            return kv == 2 ? launch_reg<2, 512>(a, nb, s) : launch_reg<3, 512>(a, nb, s);
+    }
     int threads = static_cast<int>(X < kMaxThreads ? X : kMaxThreads);
     threads = ((threads + 63) / 64) * 64;
     const size_t shmem = in_lds ? 2 * static_cast<size_t>(X) * sizeof(float) : 0;
