@@ -159,3 +159,46 @@ def test_strided_rows_and_empty(oracle_lib):
     empty = api.encode(torch.empty((0, N), device="cuda"), None, torch.from_numpy(C).cuda(),
                        L, k, V, T)
     assert empty.cost.numel() == 0
+
+
+# Exact ties everywhere: weights on a 1/4 grid and a codebook rounded to halves make every
+# cost exact in fp32, so many paths tie.  The kernels that take the minimum over all
+# predecessors of a group at once (generic, L=16 with k*V = 2 or 3) must reproduce the
+# oracle's lowest-index choice bit for bit.  The k*V = 4 kernel takes its minimum in two
+# 2-bit halves; on an exact tie it may keep a different path of the same cost (lowest
+# bottom pair first), so there the unique results are compared (the cost, bitwise) and
+# the path it kept is checked to be a valid optimal path.
+TIE_CASES = [
+    # L, k, V, T, M, N, split_min
+    (8, 2, 1, 32, 4, 128, False),
+    (12, 3, 1, 30, 3, 90, False),
+    (16, 2, 1, 64, 3, 192, False),
+    (16, 3, 1, 64, 2, 128, False),
+    (16, 2, 2, 64, 3, 192, True),
+    (16, 4, 1, 32, 2, 64, True),
+]
+
+
+@pytest.mark.parametrize("L,k,V,T,M,N,split_min", TIE_CASES)
+@pytest.mark.parametrize("weighted", [False, True])
+def test_exact_ties(oracle_lib, L, k, V, T, M, N, split_min, weighted):
+    _say(f"ties L={L} k={k} V={V} T={T} weighted={weighted}")
+    rng = np.random.default_rng(L * 100 + k * 10 + V + weighted)
+    W = (np.round(rng.standard_normal((M, N)) * 4) / 4).astype(np.float32)
+    d = (rng.integers(1, 4, N).astype(np.float32)) if weighted else None
+    C = (np.round(oracle_lib.make_codebook(L, V, 3) * 2) / 2).astype(np.float32)
+    bits, s0, cost, _ = _gpu_encode(W, d, C, L, k, V, T)
+    nb = M * (N // T)
+    ob, os0, oc = oracle_lib.encode_matrix(W, d, C, L, k, V, T, threads=THREADS)
+    assert np.array_equal(cost.view(np.uint32), oc.view(np.uint32))
+    if not split_min:
+        assert np.array_equal(bits, ob) and np.array_equal(s0, os0)
+        return
+    per_row = N // T
+    for b in range(nb):
+        r, c = divmod(b, per_row)
+        wb = W[r, c * T:(c + 1) * T]
+        db = None if d is None else d[c * T:(c + 1) * T]
+        assert int(s0[b]) < (1 << (L - k * V))
+        g_path = oracle_lib.path_cost(wb, db, C, L, k, V, T, bits[b], int(s0[b]))
+        assert g_path.view(np.uint32) == oc[b].view(np.uint32)
