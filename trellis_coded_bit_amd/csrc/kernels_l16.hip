@@ -104,13 +104,8 @@ __device__ __forceinline__ void acs_group(uint32_t (&J)[kRegs], float4 (&ring)[k
     constexpr int r0 = phys(NM, group_reg(P, g, 0)), r1 = phys(NM, group_reg(P, g, 1));
     constexpr int r2 = phys(NM, group_reg(P, g, 2)), r3 = phys(NM, group_reg(P, g, 3));
     const uint32_t u0 = J[r0], u1 = J[r1], u2 = J[r2], u3 = J[r3];
-    const uint32_t m01 = u0 < u1 ? u0 : u1;
-    const uint32_t m23 = u2 < u3 ? u2 : u3;
-    const uint32_t mu = m01 < m23 ? m01 : m23;
-    const uint64_t c01 = __ballot(u1 < u0);
-    const uint64_t c23 = __ballot(u3 < u2);
-    const uint64_t chi = __ballot(m23 < m01);
-    const uint64_t b0 = (chi & c23) | (~chi & c01);
+    uint64_t chi, b0;
+    const uint32_t mu = argmin4(u0, u1, u2, u3, chi, b0);
     acc = shift_in(shift_in(acc, chi), b0);
     const float m = __uint_as_float(mu);
     const float e0 = wt - c.x, e1 = wt - c.y, e2 = wt - c.z, e3 = wt - c.w;
@@ -128,6 +123,26 @@ __device__ __forceinline__ void acs_segment_impl(uint32_t (&J)[kRegs], float4 (&
     uint32_t acc = 0;
     (acs_group<SEG, WEIGHTED, NM, I>(J, ring, rs, voff, wt, dt, acc), ...);
     *bp_word = acc;
+}
+
+// Groups I0 .. I0 + 7 of segment SEG, their backpointer bits shifted into acc (the word
+// is stored by the caller once all 16 groups are in).
+template <int SEG, bool WEIGHTED, int NM, int I0, int... I>
+__device__ __forceinline__ void acs_half_impl(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+                                              __amdgpu_buffer_rsrc_t rs, uint32_t voff, float wt,
+                                              float dt, uint32_t &acc,
+                                              std::integer_sequence<int, I...>) {
+    (acs_group<SEG, WEIGHTED, NM, I0 + I>(J, ring, rs, voff, wt, dt, acc), ...);
+}
+
+template <int SEG, bool WEIGHTED, int NM, int I0>
+__device__ __forceinline__ void acs_half(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+                                         const Ctx &cx, int t0, uint32_t &acc) {
+    constexpr int P = seg_step(SEG);
+    const int t = t0 + P - 1;
+    acs_half_impl<SEG, WEIGHTED, NM, I0>(J, ring, cx.rs, cx.voff, cx.wcol[t],
+                                         WEIGHTED ? cx.dcol[t] : 1.0f, acc,
+                                         std::make_integer_sequence<int, 8>{});
 }
 
 template <int SEG, bool WEIGHTED, int NM>
@@ -156,9 +171,14 @@ __device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[
     acs_segment<4, WEIGHTED, NM>(J, ring, cx, t0);
     __syncthreads();  // every wave has read round 1
     round_write<NM, 0>(J, cx);
-    acs_segment<5, WEIGHTED, NM>(J, ring, cx, t0);
+    // segment 5 works on the r[6] = 1 registers only, so its second half runs while the
+    // round-0 values (which refill the r[6] = 0 registers) are on their way in
+    uint32_t acc5 = 0;
+    acs_half<5, WEIGHTED, NM, 0>(J, ring, cx, t0, acc5);
     __syncthreads();  // round-0 values written by every wave
     round_read<NM, 0>(J, cx);
+    acs_half<5, WEIGHTED, NM, 8>(J, ring, cx, t0, acc5);
+    cx.bp[2 * kThreads * (t0 + 2) + seg_half(5)] = acc5;
     __syncthreads();  // every wave has read round 0
     round_write<NM, 1>(J, cx);
 }

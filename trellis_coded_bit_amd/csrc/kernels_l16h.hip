@@ -92,13 +92,8 @@ __device__ __forceinline__ void acsh_group_plain(uint32_t (&J)[kRegs], uint32_t 
     constexpr int r0 = phys(NM, group_reg(P, g, 0)), r1 = phys(NM, group_reg(P, g, 1));
     constexpr int r2 = phys(NM, group_reg(P, g, 2)), r3 = phys(NM, group_reg(P, g, 3));
     const uint32_t u0 = J[r0], u1 = J[r1], u2 = J[r2], u3 = J[r3];
-    const uint32_t m01 = u0 < u1 ? u0 : u1;
-    const uint32_t m23 = u2 < u3 ? u2 : u3;
-    const uint32_t mu = m01 < m23 ? m01 : m23;
-    const uint64_t c01 = __ballot(u1 < u0);
-    const uint64_t c23 = __ballot(u3 < u2);
-    const uint64_t chi = __ballot(m23 < m01);
-    const uint64_t b0 = (chi & c23) | (~chi & c01);
+    uint64_t chi, b0;
+    const uint32_t mu = argmin4(u0, u1, u2, u3, chi, b0);
     acc = shift_in(shift_in(acc, chi), b0);
     J[r0] = mu;
     J[r1] = mu;
@@ -131,13 +126,8 @@ __device__ __forceinline__ void acsh_group_metric(uint32_t (&J)[kRegs],
     constexpr int r0 = phys(NM, group_reg(P, g, 0)), r1 = phys(NM, group_reg(P, g, 1));
     constexpr int r2 = phys(NM, group_reg(P, g, 2)), r3 = phys(NM, group_reg(P, g, 3));
     const uint32_t u0 = J[r0], u1 = J[r1], u2 = J[r2], u3 = J[r3];
-    const uint32_t m01 = u0 < u1 ? u0 : u1;
-    const uint32_t m23 = u2 < u3 ? u2 : u3;
-    const uint32_t mu = m01 < m23 ? m01 : m23;
-    const uint64_t c01 = __ballot(u1 < u0);
-    const uint64_t c23 = __ballot(u3 < u2);
-    const uint64_t chi = __ballot(m23 < m01);
-    const uint64_t b0 = (chi & c23) | (~chi & c01);
+    uint64_t chi, b0;
+    const uint32_t mu = argmin4(u0, u1, u2, u3, chi, b0);
     acc = shift_in(shift_in(acc, chi), b0);
     float a0 = __uint_as_float(mu), a1 = a0, a2 = a0, a3 = a0;
 #pragma unroll

@@ -23,6 +23,23 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t acc, uint64_t mask) {
     return r;
 }
 
+// Minimum of four cost patterns and the index j of its first occurrence (the lowest j on
+// ties), as two wave-wide bit masks: hi = j >> 1, lo = j & 1.  Two VALU minimums and
+// three equality compares (into SGPR masks); the index bits are assembled on the SALU:
+//   j = 0 if u0 is the minimum, else 1 if u1 is, else 2 if u2 is, else 3.
+__device__ __forceinline__ uint32_t argmin4(uint32_t u0, uint32_t u1, uint32_t u2, uint32_t u3,
+                                            uint64_t &hi, uint64_t &lo) {
+    const uint32_t m01 = u0 < u1 ? u0 : u1;  // the backend fuses these two into v_min3
+    const uint32_t m3 = m01 < u2 ? m01 : u2;
+    const uint32_t mu = m3 < u3 ? m3 : u3;
+    const uint64_t e0 = __ballot(u0 == mu);
+    const uint64_t e1 = __ballot(u1 == mu);
+    const uint64_t e2 = __ballot(u2 == mu);
+    hi = ~(e0 | e1);
+    lo = ~e0 & (e1 | ~e2);
+    return mu;
+}
+
 // Per-block context shared by the segments and transposition rounds.
 struct Ctx {
     __amdgpu_buffer_rsrc_t rs;  // wave's part of the codebook copies
