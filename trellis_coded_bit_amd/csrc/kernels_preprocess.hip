@@ -131,8 +131,17 @@ __global__ __launch_bounds__(256) void col_partial_kernel(
     if (c >= N) return;
     const int64_t r0 = static_cast<int64_t>(blockIdx.y) * slab_rows;
     const int64_t r1 = (r0 + slab_rows < M) ? r0 + slab_rows : M;
+    // rows in ascending order; loads of 8 rows are issued before their sums
     float s = 0.0f;
-    for (int64_t r = r0; r < r1; ++r) {
+    int64_t r = r0;
+    for (; r + 8 <= r1; r += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = W[(r + i) * ldw + c] / a[r + i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = __builtin_fmaf(v[i], v[i], s);
+    }
+    for (; r < r1; ++r) {
         const float v = W[r * ldw + c] / a[r];
         s = __builtin_fmaf(v, v, s);
     }
@@ -144,8 +153,17 @@ __global__ __launch_bounds__(256) void col_finalize_kernel(const float *__restri
                                                            float *__restrict__ b) {
     const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (c >= N) return;
+    // slab sums in ascending order; loads of 8 slabs are issued before their sums
     float s = 0.0f;
-    for (int i = 0; i < nslabs; ++i) s += part[static_cast<int64_t>(i) * N + c];
+    int i = 0;
+    for (; i + 8 <= nslabs; i += 8) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = part[static_cast<int64_t>(i + q) * N + c];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s += v[q];
+    }
+    for (; i < nslabs; ++i) s += part[static_cast<int64_t>(i) * N + c];
     b[c] = s > 0.0f ? __builtin_sqrtf(s / static_cast<float>(M)) : 1.0f;
 }
 
