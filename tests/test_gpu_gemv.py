@@ -71,6 +71,8 @@ CASES = [
     (16, 1, 1, 17, 3, 17 * 61),
     (12, 3, 2, 32, 3, 128),
     (16, 2, 1, 256, 70, 256),
+    (12, 2, 1, 64, 4500, 512),   # many short rows: two rows per wave
+    (16, 4, 1, 256, 9, 2048),
 ]
 
 
