@@ -94,6 +94,17 @@ def measured_traffic(workload_name):
     return None
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, W, d, C, nblocks, threads):
     import oracle
     rng = np.random.default_rng(12345)
@@ -107,7 +118,7 @@ def cpu_baseline(w, W, d, C, nblocks, threads):
     oracle.encode_matrix(W, d, C, w.L, w.k, w.V, w.T, blocks=one, threads=1)
     dt1 = time.perf_counter() - t1
     return {"value": blocks.size * w.T / dt, "unit": "weights/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(),
             "sample": f"{blocks.size} seeded-random blocks of the same workload "
                       f"({blocks.size * w.T} weights), one block per thread at a time, "
                       f"{dt:.2f} s wall",
@@ -209,8 +220,26 @@ def bcjr_bench(torch, _lib, w, Wt, dt_, Ct, tau, steps):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / steps
     updates = w.blocks * (w.T // w.V) * (1 << w.L)
+    slots = bcjr_slots_per_state(w.k * w.V, w.V)
+    rate = updates / (ms / 1e3)
     return {"tau": tau, "ms": ms, "weights_per_s": w.weights / (ms / 1e3),
-            "state_updates_per_s_per_pass": updates / (ms / 1e3)}
+            "state_updates_per_s_per_pass": rate, "valu_slots_per_state": slots,
+            "valu_pct": 100.0 * rate * slots / VALU_PEAK_OPS}
+
+
+def bcjr_slots_per_state(kv, V):
+    """Algorithmic VALU issue slots per state for the forward and the backward pass
+    together, G = 2^kv states per group, a transcendental (exp2, log2) counted as 2 slots
+    (its measured issue cost on gfx950).
+    Forward, per state: per coordinate w - c, its square and the fma into the log-weight
+    (3V); the group maximum and the sum ((G-1)/G each); the subtraction of the maximum
+    and exp2 (1 + 2); per group log2, + maximum, - shift ((2 + 2)/G).
+    Backward: the same, plus per coordinate the numerator fma (V), plus per group the
+    group weight (+ F, exp2 and the two fmas into numerator and denominator: (1 + 2 + 2)/G)."""
+    G = 1 << kv
+    fwd = 3 * V + 2 * (G - 1) / G + 3 + 4 / G
+    bwd = fwd + V + 5 / G
+    return fwd + bwd
 
 
 def preprocess_bench(torch, _lib, w, Wt, iters):

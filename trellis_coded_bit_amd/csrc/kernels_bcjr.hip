@@ -3,9 +3,10 @@
 // the soft codeword is the Boltzmann expectation of the emitted values over all trellis
 // paths, and the hard code comes back as the temperature goes to 0.
 //
-// Energy of a path = the weighted squared error the Viterbi search minimises, with the
-// same fp32 branch metric chain; probability of a path = exp(-J/tau) / Z.  Work is in
-// base-2 logs: g(s) = m(s) * ns with ns = -log2(e)/tau.
+// Energy of a path = the weighted squared error the Viterbi search minimises; probability
+// of a path = exp(-J/tau) / Z.  Work is in base-2 logs: the log-weight of state s at a
+// step is g(s) = sum_v d_v * e_v^2 * ns with e_v = w_v - C[s][v] and ns = -log2(e)/tau,
+// added to the incoming vector value in fp32 as one fma per coordinate.
 //
 // Group form used here (x = a group of 2^kv states that share predecessors):
 //  - forward:  F_t(x) = LSE_j [g_t(s_j) + F_{t-1}(s_j >> kv)], s_j = (j << (L-kv)) | x,
@@ -52,13 +53,14 @@ struct BcjrArgs {
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ float metric(const float *wv, const float *dv, const float *c, int V,
-                                        bool weighted) {
-    float acc = 0.0f;
+// base + g(s) in base-2 log units: g(s) = sum_v d_v * (w_v - c_v)^2 * ns, evaluated as
+// the chain acc = base, acc = fmaf(fl(e_v * e_v), dn_v, acc) over v, dn_v = fl(d_v * ns).
+__device__ __forceinline__ float add_log_weight(float base, const float *wv, const float *dn,
+                                                const float *c, int V) {
+    float acc = base;
     for (int v = 0; v < V; ++v) {
         const float e = wv[v] - c[v];
-        const float de = weighted ? dv[v] * e : e;
-        acc = __builtin_fmaf(de, e, acc);
+        acc = __builtin_fmaf(e * e, dn[v], acc);
     }
     return acc;
 }
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(max_threads(KV)) void bcjr_kernel(BcjrArgs a) {
     float *Fc = bufA;
     float *Fn = bufB;
     double offset = 0.0;  // sum of the shifts, base-2 log
-    float wv[TCQ_MAX_V], dv[TCQ_MAX_V];
+    float wv[TCQ_MAX_V], dn[TCQ_MAX_V];
     for (int t = 1; t <= n; ++t) {
         float c = 0.0f;
         if (t >= 2) {
@@ -151,21 +153,22 @@ __global__ __launch_bounds__(max_threads(KV)) void bcjr_kernel(BcjrArgs a) {
         }
         for (int v = 0; v < V; ++v) {
             wv[v] = w[(t - 1) * V + v];
-            dv[v] = weighted ? dd[(t - 1) * V + v] : 1.0f;
+            dn[v] = (weighted ? dd[(t - 1) * V + v] : 1.0f) * ns;
         }
         float lmax = kNegInf;
         for (int64_t x = tid; x < X; x += nt) {
             float val[G];
-            float mx = kNegInf;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 const int64_t s = (static_cast<int64_t>(j) << sh) | x;
-                val[j] = metric(wv, dv, a.C + s * V, V, weighted) * ns + Fc[s >> KV];
-                mx = fmaxf(mx, val[j]);
+                val[j] = add_log_weight(Fc[s >> KV], wv, dn, a.C + s * V, V);
             }
-            float sum = 0.0f;
+            float mx = val[0];
 #pragma unroll
-            for (int j = 0; j < G; ++j) sum += exp2_(val[j] - mx);
+            for (int j = 1; j < G; ++j) mx = fmaxf(mx, val[j]);
+            float sum = exp2_(val[0] - mx);
+#pragma unroll
+            for (int j = 1; j < G; ++j) sum += exp2_(val[j] - mx);
             const float f = mx + log2_(sum) - c;
             Fn[x] = f;
             if (t < n) fst[static_cast<int64_t>(t) * X + x] = f;
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(max_threads(KV)) void bcjr_kernel(BcjrArgs a) {
         }
         for (int v = 0; v < V; ++v) {
             wv[v] = w[(t - 1) * V + v];
-            dv[v] = weighted ? dd[(t - 1) * V + v] : 1.0f;
+            dn[v] = (weighted ? dd[(t - 1) * V + v] : 1.0f) * ns;
         }
         Expect ex;
         ex.u = kNegInf;
@@ -227,13 +230,14 @@ __global__ __launch_bounds__(max_threads(KV)) void bcjr_kernel(BcjrArgs a) {
         for (int64_t x = tid; x < X; x += nt) {
             const float fx = fst[static_cast<int64_t>(t - 1) * X + x];
             float val[G];
-            float mx = kNegInf;
 #pragma unroll
             for (int b = 0; b < G; ++b) {
                 const int64_t s2 = (x << KV) | b;
-                val[b] = metric(wv, dv, a.C + s2 * V, V, weighted) * ns + Bc[s2 & lowmask];
-                mx = fmaxf(mx, val[b]);
+                val[b] = add_log_weight(Bc[s2 & lowmask], wv, dn, a.C + s2 * V, V);
             }
+            float mx = val[0];
+#pragma unroll
+            for (int b = 1; b < G; ++b) mx = fmaxf(mx, val[b]);
             float sum = 0.0f;
             float gnum[TCQ_MAX_V];
             for (int v = 0; v < V; ++v) gnum[v] = 0.0f;
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
             offset += static_cast<double>(c);
         }
         const float wt = w[t - 1];
-        const float dt = weighted ? dd[t - 1] : 1.0f;
+        const float dn = (weighted ? dd[t - 1] : 1.0f) * ns;
         float lmax = kNegInf;
 #pragma unroll
         for (int iy = 0; iy < kMaxNY; ++iy) {
@@ -371,17 +375,17 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
 #pragma unroll
             for (int b = 0; b < G; ++b) {
                 float val[G];
-                float mx = kNegInf;
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
                     const float e = wt - creg[iy][j][b];
-                    const float m = __builtin_fmaf(weighted ? dt * e : e, e, 0.0f);
-                    val[j] = m * ns + fj[j];
-                    mx = fmaxf(mx, val[j]);
+                    val[j] = __builtin_fmaf(e * e, dn, fj[j]);
                 }
-                float sum = 0.0f;
+                float mx = val[0];
 #pragma unroll
-                for (int j = 0; j < G; ++j) sum += exp2_(val[j] - mx);
+                for (int j = 1; j < G; ++j) mx = fmaxf(mx, val[j]);
+                float sum = exp2_(val[0] - mx);
+#pragma unroll
+                for (int j = 1; j < G; ++j) sum += exp2_(val[j] - mx);
                 fo[b] = mx + log2_(sum) - c;
                 lmax = fmaxf(lmax, fo[b]);
             }
@@ -436,8 +440,10 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
             for (int i = 1; i < nwaves; ++i) c = fmaxf(c, part_max[(t + 1) & 1][i]);
         }
         const float wt = w[t - 1];
-        const float dt = weighted ? dd[t - 1] : 1.0f;
-        float eu = kNegInf, enum_ = 0.0f, eden = 0.0f;
+        const float dn = (weighted ? dd[t - 1] : 1.0f) * ns;
+        // (eu, enum_, eden) stands for (2^eu enum_, 2^eu eden); every term is finite, so
+        // the first y initialises it and later ones merge into it
+        float eu = 0.0f, enum_ = 0.0f, eden = 0.0f;
         float lmax = kNegInf;
 #pragma unroll
         for (int iy = 0; iy < kMaxNY; ++iy) {
@@ -446,22 +452,24 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
             float bb[G];
 #pragma unroll
             for (int b = 0; b < G; ++b) bb[b] = Bc[pad((y << KV) | b)];
+            float gu[G], gs[G], gn[G];  // per group: log2 weight, softmax sum, numerator
 #pragma unroll
             for (int j = 0; j < G; ++j) {
                 const int64_t xg = (static_cast<int64_t>(j) << shY) | y;
                 const float fx = fst[static_cast<int64_t>(t - 1) * X + xg];
                 float val[G];
-                float mx = kNegInf;
 #pragma unroll
                 for (int b = 0; b < G; ++b) {
                     const float e = wt - creg[iy][j][b];
-                    const float m = __builtin_fmaf(weighted ? dt * e : e, e, 0.0f);
-                    val[b] = m * ns + bb[b];
-                    mx = fmaxf(mx, val[b]);
+                    val[b] = __builtin_fmaf(e * e, dn, bb[b]);
                 }
-                float sum = 0.0f, gnum = 0.0f;
+                float mx = val[0];
 #pragma unroll
-                for (int b = 0; b < G; ++b) {
+                for (int b = 1; b < G; ++b) mx = fmaxf(mx, val[b]);
+                float sum = exp2_(val[0] - mx);
+                float gnum = sum * creg[iy][j][0];
+#pragma unroll
+                for (int b = 1; b < G; ++b) {
                     const float e = exp2_(val[b] - mx);
                     sum += e;
                     gnum = __builtin_fmaf(e, creg[iy][j][b], gnum);
@@ -471,12 +479,32 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
                     Bn[pad(xg)] = bnew;
                     lmax = fmaxf(lmax, bnew);
                 }
-                const float gu = mx + fx;
-                const float nm = fmaxf(eu, gu);
-                const float sa = (eu == kNegInf) ? 0.0f : exp2_(eu - nm);
-                const float sb = exp2_(gu - nm);
-                enum_ = enum_ * sa + gnum * sb;
-                eden = eden * sa + sum * sb;
+                gu[j] = mx + fx;
+                gs[j] = sum;
+                gn[j] = gnum;
+            }
+            // the G groups of this y against their own maximum, then into the running sum
+            float lu = gu[0];
+#pragma unroll
+            for (int j = 1; j < G; ++j) lu = fmaxf(lu, gu[j]);
+            float sc = exp2_(gu[0] - lu);
+            float ln = gn[0] * sc, ld = gs[0] * sc;
+#pragma unroll
+            for (int j = 1; j < G; ++j) {
+                sc = exp2_(gu[j] - lu);
+                ln = __builtin_fmaf(gn[j], sc, ln);
+                ld = __builtin_fmaf(gs[j], sc, ld);
+            }
+            if (iy == 0) {
+                eu = lu;
+                enum_ = ln;
+                eden = ld;
+            } else {
+                const float nm = fmaxf(eu, lu);
+                const float sa = exp2_(eu - nm);
+                const float sb = exp2_(lu - nm);
+                enum_ = __builtin_fmaf(enum_, sa, ln * sb);
+                eden = __builtin_fmaf(eden, sa, ld * sb);
                 eu = nm;
             }
         }
