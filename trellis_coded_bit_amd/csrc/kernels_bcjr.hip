@@ -285,39 +285,46 @@ __global__ __launch_bounds__(max_threads(KV)) void bcjr_kernel(BcjrArgs a) {
     }
 }
 
-// Register-codebook variant for V = 1 (L - 2 kv >= log2(NT)).  Thread tid owns the y
-// values y_i = tid + NT i (i < NY), and with them the states
+// Register-codebook variant for L = 16, V = 1, kv = 2 or 3.  Thread tid owns the y values
+// y_i = tid + NT i (i < NY), and with them the states
 //     s = (j << (L - kv)) | (y << kv) | b,   j, b < 2^kv.
 // In the forward pass these are the predecessors of its groups x = (y << kv) | b; in the
 // backward pass they are the successors of its groups x' = (j << (L - 2 kv)) | y.  So the
 // thread's codebook values never change and stay in registers for the whole block, and
 // the G forward values F(s >> kv) (or backward values B(s mod 2^(L-kv))) that a y needs
 // are read from LDS once and shared by its G groups.  LDS vectors are padded by one
-// float every 32 to spread the strided accesses over the banks.
-__device__ __forceinline__ int pad(int64_t i) { return static_cast<int>(i + (i >> 5)); }
+// float every 32 to spread the strided accesses over the banks.  With L fixed, every LDS
+// and workspace index is a per-lane base plus a compile-time offset.
+__host__ __device__ constexpr int pad(int i) { return i + (i >> 5); }
 // y values per thread that fit in registers (NY G^2 codebook floats)
 constexpr int reg_max_ny(int kv) { return kv == 2 ? 8 : 2; }
 
 template <int KV, int NT>
 __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
     extern __shared__ float lds[];
+    // the block's weights and d, read through LDS so that no per-step vector-memory
+    // wait drains the workspace loads in flight
+    __shared__ float wsh[TCQ_MAX_STEPS], dsh[TCQ_MAX_STEPS];
     __shared__ float part_max[2][kMaxWaves];
     __shared__ float part_m[kMaxWaves], part_s[kMaxWaves];
     __shared__ float part_u[2][kMaxWaves];
     __shared__ float part_num[2][kMaxWaves];
     __shared__ float part_den[2][kMaxWaves];
 
+    constexpr int L = 16;
     constexpr int G = 1 << KV;
     constexpr int nwaves = NT / 64;
+    constexpr int X = 1 << (L - KV);  // groups per step
+    constexpr int shF = L - KV;       // j position in a state
+    constexpr int shY = L - 2 * KV;   // j position in a backward group
+    constexpr int NY = (1 << shY) / NT;
+    constexpr int PX = pad(X);        // padded vector length
+    static_assert(NY >= 1 && NY * NT == (1 << shY) && NY <= reg_max_ny(KV), "y split");
+    static_assert(NT % 32 == 0 && shY >= 5, "padding splits into base + offset");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int L = a.L;
     const int n = a.n;
-    const int64_t X = int64_t{1} << (L - KV);
-    const int shF = L - KV;      // j position in a state
-    const int shY = L - 2 * KV;  // j position in a backward group
-    const int NY = static_cast<int>((int64_t{1} << shY) / NT);
     const int64_t blk = a.block0 + blockIdx.x;
     const int64_t row = blk / a.blocks_per_row;
     const int64_t col = blk % a.blocks_per_row;
@@ -325,28 +332,31 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
     const float *dd = a.d ? a.d + col * n : nullptr;
     const bool weighted = a.d != nullptr;
     float *fst = a.fstore + static_cast<int64_t>(blockIdx.x) * a.fstore_per_block;
-    const int64_t padded = X + (X >> 5);
     float *bufA = lds;
-    float *bufB = lds + padded;
+    float *bufB = lds + PX;
     const float ns = a.ns;
+    // per-lane parts of the padded indices: pad(A + B) = pad(A) + pad(B) when A is a
+    // multiple of 32
+    const int pT = pad(tid);       // y_i = tid + NT i, groups (j << shY) | y_i
+    const int pG = pad(tid << KV); // groups (y_i << KV) | b: pad(.) = pG + b + const
 
-    constexpr int kMaxNY = reg_max_ny(KV);
-    float creg[kMaxNY][G][G];
+    float creg[NY][G][G];
 #pragma unroll
-    for (int iy = 0; iy < kMaxNY; ++iy) {
-        if (iy < NY) {
-            const int64_t y = tid + static_cast<int64_t>(NT) * iy;
+    for (int i = 0; i < NY; ++i) {
 #pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const float *src = a.C + ((static_cast<int64_t>(j) << shF) | (y << KV));
+        for (int j = 0; j < G; ++j) {
+            const float *src = a.C + ((j << shF) | ((tid + NT * i) << KV));
 #pragma unroll
-                for (int b = 0; b < G; ++b) creg[iy][j][b] = src[b];
-            }
+            for (int b = 0; b < G; ++b) creg[i][j][b] = src[b];
         }
     }
-    for (int64_t x = tid; x < X; x += NT) {
+    for (int x = tid; x < X; x += NT) {
         bufA[pad(x)] = 0.0f;
         fst[x] = 0.0f;  // F_0
+    }
+    for (int t = tid; t < n; t += NT) {
+        wsh[t] = w[t];
+        dsh[t] = (weighted ? dd[t] : 1.0f) * ns;
     }
     __syncthreads();
 
@@ -361,23 +371,22 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
             for (int i = 1; i < nwaves; ++i) c = fmaxf(c, part_max[(t - 1) & 1][i]);
             offset += static_cast<double>(c);
         }
-        const float wt = w[t - 1];
-        const float dn = (weighted ? dd[t - 1] : 1.0f) * ns;
+        const float wt = wsh[t - 1];
+        const float dn = dsh[t - 1];
+        float4 *frow = reinterpret_cast<float4 *>(fst + static_cast<int64_t>(t) * X);
         float lmax = kNegInf;
 #pragma unroll
-        for (int iy = 0; iy < kMaxNY; ++iy) {
-            if (iy >= NY) break;
-            const int64_t y = tid + static_cast<int64_t>(NT) * iy;
+        for (int i = 0; i < NY; ++i) {
             float fj[G];
 #pragma unroll
-            for (int j = 0; j < G; ++j) fj[j] = Fc[pad((static_cast<int64_t>(j) << shY) | y)];
+            for (int j = 0; j < G; ++j) fj[j] = Fc[pT + pad(NT * i) + pad(j << shY)];
             float fo[G];
 #pragma unroll
             for (int b = 0; b < G; ++b) {
                 float val[G];
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
-                    const float e = wt - creg[iy][j][b];
+                    const float e = wt - creg[i][j][b];
                     val[j] = __builtin_fmaf(e * e, dn, fj[j]);
                 }
                 float mx = val[0];
@@ -389,12 +398,14 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
                 fo[b] = mx + log2_(sum) - c;
                 lmax = fmaxf(lmax, fo[b]);
             }
-            const int64_t x0 = y << KV;
 #pragma unroll
-            for (int b = 0; b < G; ++b) Fn[pad(x0 + b)] = fo[b];
+            for (int b = 0; b < G; ++b) Fn[pG + b + pad((NT * i) << KV)] = fo[b];
             if (t < n) {
+                // groups ((tid + NT i) << KV) + b, b < G: G / 4 float4 per thread
 #pragma unroll
-                for (int b = 0; b < G; ++b) fst[static_cast<int64_t>(t) * X + x0 + b] = fo[b];
+                for (int q = 0; q < G / 4; ++q)
+                    frow[((NT * i) << KV) / 4 + tid * (G / 4) + q] =
+                        make_float4(fo[4 * q], fo[4 * q + 1], fo[4 * q + 2], fo[4 * q + 3]);
             }
         }
         lmax = wave_max(lmax);
@@ -406,7 +417,7 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
     }
     {
         float m = kNegInf, s2 = 0.0f;
-        for (int64_t x = tid; x < X; x += NT) lse_merge(m, s2, Fc[pad(x)], 1.0f);
+        for (int x = tid; x < X; x += NT) lse_merge(m, s2, Fc[pad(x)], 1.0f);
         for (int off = 32; off >= 1; off >>= 1) {
             const float om = __shfl_xor(m, off);
             const float os = __shfl_xor(s2, off);
@@ -430,7 +441,24 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
     // ---------------- backward ----------------
     float *Bc = bufA;
     float *Bn = bufB;
-    for (int64_t x = tid; x < X; x += NT) Bc[pad(x)] = 0.0f;
+    for (int x = tid; x < X; x += NT) Bc[pad(x)] = 0.0f;
+    // F_{t-1} at the thread's backward groups (j << shY) | y_i, consumed in the order
+    // p = G i + j (NP per step) and requested kRing positions ahead of use, across the
+    // step boundary (the last step requests row 0 again; those values go unused)
+    constexpr int NP = NY * G;
+    constexpr int kRing = NP / 2;
+    // raw buffer loads over the block's n rows: one per-lane offset (4 * tid) for every
+    // load, the row and position in the scalar offset
+    const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
+        fst, 0, n * X * static_cast<int>(sizeof(float)), 0x00020000);
+    const int voff = tid * static_cast<int>(sizeof(float));
+    auto fload = [&](int r, int q) {
+        const int soff = (r * X + ((q % G) << shY) + NT * (q / G)) * static_cast<int>(sizeof(float));
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(frs, voff, soff, 0));
+    };
+    float ring[kRing];
+#pragma unroll
+    for (int p = 0; p < kRing; ++p) ring[p] = fload(n - 1, p);
     __syncthreads();
     float *out = a.soft + row * a.ldo + col * n;
     for (int t = n; t >= 1; --t) {
@@ -439,47 +467,51 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
             c = part_max[(t + 1) & 1][0];
             for (int i = 1; i < nwaves; ++i) c = fmaxf(c, part_max[(t + 1) & 1][i]);
         }
-        const float wt = w[t - 1];
-        const float dn = (weighted ? dd[t - 1] : 1.0f) * ns;
+        const float wt = wsh[t - 1];
+        const float dn = dsh[t - 1];
+        const int nrow = t >= 2 ? t - 2 : 0;
         // (eu, enum_, eden) stands for (2^eu enum_, 2^eu eden); every term is finite, so
         // the first y initialises it and later ones merge into it
         float eu = 0.0f, enum_ = 0.0f, eden = 0.0f;
         float lmax = kNegInf;
 #pragma unroll
-        for (int iy = 0; iy < kMaxNY; ++iy) {
-            if (iy >= NY) break;
-            const int64_t y = tid + static_cast<int64_t>(NT) * iy;
+        for (int i = 0; i < NY; ++i) {
             float bb[G];
 #pragma unroll
-            for (int b = 0; b < G; ++b) bb[b] = Bc[pad((y << KV) | b)];
+            for (int b = 0; b < G; ++b) bb[b] = Bc[pG + b + pad((NT * i) << KV)];
             float gu[G], gs[G], gn[G];  // per group: log2 weight, softmax sum, numerator
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const int64_t xg = (static_cast<int64_t>(j) << shY) | y;
-                const float fx = fst[static_cast<int64_t>(t - 1) * X + xg];
                 float val[G];
 #pragma unroll
                 for (int b = 0; b < G; ++b) {
-                    const float e = wt - creg[iy][j][b];
+                    const float e = wt - creg[i][j][b];
                     val[b] = __builtin_fmaf(e * e, dn, bb[b]);
                 }
                 float mx = val[0];
 #pragma unroll
                 for (int b = 1; b < G; ++b) mx = fmaxf(mx, val[b]);
                 float sum = exp2_(val[0] - mx);
-                float gnum = sum * creg[iy][j][0];
+                float gnum = sum * creg[i][j][0];
 #pragma unroll
                 for (int b = 1; b < G; ++b) {
                     const float e = exp2_(val[b] - mx);
                     sum += e;
-                    gnum = __builtin_fmaf(e, creg[iy][j][b], gnum);
+                    gnum = __builtin_fmaf(e, creg[i][j][b], gnum);
                 }
-                if (t > 1) {
-                    const float bnew = mx + log2_(sum) - c;
-                    Bn[pad(xg)] = bnew;
-                    lmax = fmaxf(lmax, bnew);
+                // B_{t-1}; on the last step (t = 1) it lands in the unused buffer
+                const float bnew = mx + log2_(sum) - c;
+                Bn[pT + pad(NT * i) + pad(j << shY)] = bnew;
+                lmax = fmaxf(lmax, bnew);
+                const int pos = G * i + j;
+                gu[j] = mx + ring[pos % kRing];
+                {
+                    const int q = pos + kRing;  // position requested now
+                    // keep the request here: the scheduler would otherwise sink it towards
+                    // its use and shorten the distance the ring is meant to cover
+                    __builtin_amdgcn_sched_barrier(0);
+                    ring[pos % kRing] = q < NP ? fload(t - 1, q) : fload(nrow, q - NP);
                 }
-                gu[j] = mx + fx;
                 gs[j] = sum;
                 gn[j] = gnum;
             }
@@ -495,7 +527,7 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
                 ln = __builtin_fmaf(gn[j], sc, ln);
                 ld = __builtin_fmaf(gs[j], sc, ld);
             }
-            if (iy == 0) {
+            if (i == 0) {
                 eu = lu;
                 enum_ = ln;
                 eden = ld;
@@ -551,8 +583,7 @@ __global__ __launch_bounds__(NT) void bcjr_reg_kernel(BcjrArgs a) {
 
 template <int KV, int NT>
 hipError_t launch_reg(const BcjrArgs &a, int64_t nb, hipStream_t s) {
-    const int64_t X = int64_t{1} << (a.L - KV);
-    const size_t shmem = 2 * static_cast<size_t>(X + (X >> 5)) * sizeof(float);
+    const size_t shmem = 2 * static_cast<size_t>(pad(1 << (16 - KV))) * sizeof(float);
     auto kern = bcjr_reg_kernel<KV, NT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -630,15 +661,10 @@ hipError_t launch_bcjr(const float *W, int64_t ldw, const float *d, const float 
     a.soft = soft;
     a.ldo = ldo;
     a.logz = logz;
-    // register-codebook kernel: V = 1, 2^(L - 2 kv) a multiple of the workgroup size,
-    // at most 4 y values per thread, vectors in LDS
-    if (V == 1 && in_lds && (kv == 2 || kv == 3)) {
-        const int nt = 512;
-        const int64_t ys = int64_t{1} << (L - 2 * kv);
-        const size_t need = 2 * static_cast<size_t>(X + (X >> 5)) * sizeof(float);
-        if (ys % nt == 0 && ys / nt <= reg_max_ny(kv) && need <= kBcjrLdsBytes + (8u << 10))
-            return kv == 2 ? launch_reg<2, 512>(a, nb, s) : launch_reg<3, 512>(a, nb, s);
-    }
+    // register-codebook kernel: L = 16, V = 1, kv = 2 (8 y values per thread) or 3 (2);
+    // its two padded vectors (132 KiB at kv = 2) sit in LDS
+    if (L == 16 && V == 1 && (kv == 2 || kv == 3))
+        return kv == 2 ? launch_reg<2, 512>(a, nb, s) : launch_reg<3, 512>(a, nb, s);
     int threads = static_cast<int>(X < kMaxThreads ? X : kMaxThreads);
     threads = ((threads + 63) / 64) * 64;
     const size_t shmem = in_lds ? 2 * static_cast<size_t>(X) * sizeof(float) : 0;
