@@ -30,6 +30,11 @@ namespace {
 
 using namespace l16;
 
+// The shared per-block context plus backpointer stores through a buffer descriptor.
+struct CtxH : Ctx {
+    BpBuf bpb;
+};
+
 // Codebook copies: for step P (1..3) and coordinate v, per (wave, group, lane) one float4
 // with coordinate v of the group's four successors: 3 V copies of kCopy float4.
 template <int V>
@@ -148,8 +153,8 @@ __device__ __forceinline__ void acsh_group_metric(uint32_t (&J)[kRegs],
 template <int SEG, bool WEIGHTED, int NM, int V, int MP, int... I>
 __device__ __forceinline__ void acsh_segment_impl(uint32_t (&J)[kRegs],
                                                   float4 (&ring)[Ring<V>::kSize],
-                                                  const Ctx &cx, const float (&wt)[2],
-                                                  const float (&dt)[2], uint32_t *bp_word,
+                                                  const CtxH &cx, const float (&wt)[2],
+                                                  const float (&dt)[2], int bp_word,
                                                   std::integer_sequence<int, I...>) {
     uint32_t acc = 0;
     if constexpr (seg_has_metric(MP, SEG)) {
@@ -158,13 +163,13 @@ __device__ __forceinline__ void acsh_segment_impl(uint32_t (&J)[kRegs],
     } else {
         (acsh_group_plain<SEG, NM, I>(J, acc), ...);
     }
-    *bp_word = acc;
+    cx.bpb.store(bp_word, acc);
 }
 
 // Segment SEG of super-step q (half-steps 3q + 1 .. 3q + 3), pattern MP = q mod 2.
 template <int SEG, bool WEIGHTED, int NM, int V, int MP>
 __device__ __forceinline__ void acsh_segment(uint32_t (&J)[kRegs],
-                                             float4 (&ring)[Ring<V>::kSize], const Ctx &cx,
+                                             float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
                                              int h0) {
     constexpr int P = seg_step(SEG);
     const int h = h0 + P - 1;  // 0-based half-step index
@@ -178,14 +183,14 @@ __device__ __forceinline__ void acsh_segment(uint32_t (&J)[kRegs],
         }
     }
     acsh_segment_impl<SEG, WEIGHTED, NM, V, MP>(J, ring, cx, wt, dt,
-                                                cx.bp + 2 * kThreads * h + seg_half(SEG),
+                                                2 * kThreads * h + seg_half(SEG),
                                                 std::make_integer_sequence<int, 16>{});
 }
 
 // Super-step under naming NM and pattern MP; entry and exit as in kernels_l16.hip.
 template <bool WEIGHTED, int NM, int V, int MP>
 __device__ __forceinline__ void super_step_h(uint32_t (&J)[kRegs],
-                                             float4 (&ring)[Ring<V>::kSize], const Ctx &cx,
+                                             float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
                                              int h0) {
     acsh_segment<0, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
     acsh_segment<1, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
@@ -208,7 +213,7 @@ __device__ __forceinline__ void super_step_h(uint32_t (&J)[kRegs],
 // no refill.
 template <bool WEIGHTED, int V, int MP, int R>
 __device__ __forceinline__ void tail_h(uint32_t (&J)[kRegs], float4 (&ring)[Ring<V>::kSize],
-                                       const Ctx &cx, int h0) {
+                                       const CtxH &cx, int h0) {
     acsh_segment<0, WEIGHTED, 0, V, MP>(J, ring, cx, h0);
     if constexpr (R == 2) acsh_segment<1, WEIGHTED, 0, V, MP>(J, ring, cx, h0);
     __syncthreads();
@@ -245,8 +250,10 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
     const int64_t blk = block0 + blockIdx.x;
     const int64_t row = blk / blocks_per_row;
     const int64_t col = blk % blocks_per_row;
-    const Ctx cx = make_ctx(W, ldw, WEIGHTED ? d : nullptr, cb, n * V, row, col, w, l,
-                            bp + blockIdx.x * bp_per_block, 3 * V);
+    CtxH cx;
+    static_cast<Ctx &>(cx) = make_ctx(W, ldw, WEIGHTED ? d : nullptr, cb, n * V, row, col, w,
+                                      l, bp + blockIdx.x * bp_per_block, 3 * V);
+    cx.bpb = make_bpbuf(bp + blockIdx.x * bp_per_block, bp_per_block, w, l);
 
     uint32_t J[kRegs];
 #pragma unroll

@@ -62,7 +62,10 @@ __device__ __forceinline__ Ctx make_ctx(const float *W, int64_t ldw, const float
     Ctx cx;
     const uint32_t wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform
     cx.wcol = W + row * ldw + col * n;
-    cx.dcol = d ? d + col * n : nullptr;
+    // the offset, not the pointer, is selected: d keeps its provenance, so its per-step
+    // values are read with scalar loads (a vector load's wait would drain the codebook
+    // loads in flight)
+    cx.dcol = d + (d ? col * n : 0);
     // CDNA buffer descriptor word 3 (raw dword access), as used for gfx9-family parts
     cx.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float4 *>(cb + wu * (kCopy / kWaves)),
                                               0, copies * kCopy * static_cast<int>(sizeof(float4)),
@@ -83,6 +86,28 @@ __device__ __forceinline__ Ctx make_ctx(const float *W, int64_t ldw, const float
         asm volatile("" : "+v"(cx.rb[k]));
     }
     return cx;
+}
+
+// The block's backpointer words through a buffer descriptor: the lane's byte offset in a
+// VGPR and the step in the scalar offset, so that a store needs no per-step address
+// arithmetic in VGPRs.  store(word, v) has the effect of cx.bp[word] = v, `word`
+// (= 2 * kThreads * step + half) being wave-uniform.
+struct BpBuf {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t off;
+    __device__ __forceinline__ void store(int word, uint32_t v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(v, rs, static_cast<int>(off),
+                                              word * static_cast<int>(sizeof(uint32_t)), 0);
+    }
+};
+__device__ __forceinline__ BpBuf make_bpbuf(uint2 *bp_block, int64_t bp_per_block,
+                                            uint32_t w, uint32_t l) {
+    BpBuf b;
+    b.rs = __builtin_amdgcn_make_buffer_rsrc(
+        bp_block, 0, static_cast<int>(bp_per_block * static_cast<int64_t>(sizeof(uint2))),
+        0x00020000);
+    b.off = (w * kLanes + l) * static_cast<uint32_t>(sizeof(uint2));
+    return b;
 }
 
 extern __shared__ uint32_t lds_stage[];
