@@ -137,47 +137,68 @@ __device__ __forceinline__ void acs_half_impl(uint32_t (&J)[kRegs], float4 (&rin
 
 template <int SEG, bool WEIGHTED, int NM, int I0>
 __device__ __forceinline__ void acs_half(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
-                                         const Ctx &cx, int t0, uint32_t &acc) {
+                                         const Ctx &cx, const StepIn &in, uint32_t &acc) {
     constexpr int P = seg_step(SEG);
-    const int t = t0 + P - 1;
-    acs_half_impl<SEG, WEIGHTED, NM, I0>(J, ring, cx.rs, cx.voff, cx.wcol[t],
-                                         WEIGHTED ? cx.dcol[t] : 1.0f, acc,
-                                         std::make_integer_sequence<int, 8>{});
+    acs_half_impl<SEG, WEIGHTED, NM, I0>(J, ring, cx.rs, cx.voff, in.w[P - 1], in.d[P - 1],
+                                         acc, std::make_integer_sequence<int, 8>{});
 }
 
 template <int SEG, bool WEIGHTED, int NM>
 __device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
-                                            const Ctx &cx, int t0) {
+                                            const Ctx &cx, int t0, const StepIn &in) {
     constexpr int P = seg_step(SEG);
     const int t = t0 + P - 1;  // 0-based step index
-    acs_segment_impl<SEG, WEIGHTED, NM>(J, ring, cx.rs, cx.voff, cx.wcol[t],
-                                        WEIGHTED ? cx.dcol[t] : 1.0f,
+    acs_segment_impl<SEG, WEIGHTED, NM>(J, ring, cx.rs, cx.voff, in.w[P - 1], in.d[P - 1],
                                         cx.bp + 2 * kThreads * t + seg_half(SEG),
                                         std::make_integer_sequence<int, 16>{});
 }
 
-// Super-step (steps t0+1 .. t0+3) under naming NM.  On entry round 1 of the previous
-// transposition is still in LDS (the even registers already hold round 0); on exit the
-// costs have been transposed again for naming 1 - NM, with round 1 left in LDS.
+// Segment 2 (step 1 of the odd groups) with round 1 of the transposition read into the
+// registers it consumes: the four values of group i + kReadAhead are requested before
+// group i is computed, so at most 4 * (kReadAhead + 1) reads are in flight (the LDS
+// wait counter counts at most 15) and each group waits only for its own values.
+constexpr int kReadAhead = 3;
+template <bool WEIGHTED, int NM, int I>
+__device__ __forceinline__ void seg2_group(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+                                           const Ctx &cx, float wt, float dt, uint32_t &acc) {
+    if constexpr (I + kReadAhead < 16) round_read_group<1 - NM, 1, I + kReadAhead>(J, cx);
+    acs_group<2, WEIGHTED, NM, I>(J, ring, cx.rs, cx.voff, wt, dt, acc);
+}
+template <bool WEIGHTED, int NM, int... I>
+__device__ __forceinline__ void seg2_reading(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+                                             const Ctx &cx, int t0, const StepIn &in,
+                                             std::integer_sequence<int, I...>) {
+    round_read_groups<1 - NM, 1>(J, cx, std::make_integer_sequence<int, kReadAhead>{});
+    uint32_t acc = 0;
+    (seg2_group<WEIGHTED, NM, I>(J, ring, cx, in.w[0], in.d[0], acc), ...);
+    cx.bp[2 * kThreads * t0 + seg_half(2)] = acc;
+}
+
+// Super-step (steps t0+1 .. t0+3) under naming NM, with the weights (and d) of its three
+// steps in `in`; those of the next super-step are requested into `next`.  On entry
+// round 1 of the previous transposition is still in LDS (the even registers already
+// hold round 0); on exit the costs have been transposed again for naming 1 - NM, with
+// round 1 left in LDS.
 template <bool WEIGHTED, int NM>
 __device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
-                                           const Ctx &cx, int t0) {
-    acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0);
-    acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0);
+                                           const Ctx &cx, int t0, const StepIn &in,
+                                           StepIn &next) {
+    acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
+    acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0, in);
     __syncthreads();  // round-1 values written by every wave
-    round_read<1 - NM, 1>(J, cx);
-    acs_segment<2, WEIGHTED, NM>(J, ring, cx, t0);
-    acs_segment<3, WEIGHTED, NM>(J, ring, cx, t0);
-    acs_segment<4, WEIGHTED, NM>(J, ring, cx, t0);
+    seg2_reading<WEIGHTED, NM>(J, ring, cx, t0, in, std::make_integer_sequence<int, 16>{});
+    acs_segment<3, WEIGHTED, NM>(J, ring, cx, t0, in);
+    acs_segment<4, WEIGHTED, NM>(J, ring, cx, t0, in);
     __syncthreads();  // every wave has read round 1
     round_write<NM, 0>(J, cx);
     // segment 5 works on the r[6] = 1 registers only, so its second half runs while the
     // round-0 values (which refill the r[6] = 0 registers) are on their way in
     uint32_t acc5 = 0;
-    acs_half<5, WEIGHTED, NM, 0>(J, ring, cx, t0, acc5);
+    acs_half<5, WEIGHTED, NM, 0>(J, ring, cx, in, acc5);
+    next = load_steps<WEIGHTED>(cx, t0 + 3);  // complete by the barrier below
     __syncthreads();  // round-0 values written by every wave
     round_read<NM, 0>(J, cx);
-    acs_half<5, WEIGHTED, NM, 8>(J, ring, cx, t0, acc5);
+    acs_half<5, WEIGHTED, NM, 8>(J, ring, cx, in, acc5);
     cx.bp[2 * kThreads * (t0 + 2) + seg_half(5)] = acc5;
     __syncthreads();  // every wave has read round 0
     round_write<NM, 1>(J, cx);
@@ -187,14 +208,14 @@ __device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[
 // where the order departs from a full super-step).
 template <bool WEIGHTED, int NM, int R>
 __device__ __forceinline__ void tail_steps(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
-                                           const Ctx &cx, int t0) {
-    acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0);
-    if constexpr (R == 2) acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0);
+                                           const Ctx &cx, int t0, const StepIn &in) {
+    acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
+    if constexpr (R == 2) acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0, in);
     __syncthreads();
     round_read<1 - NM, 1>(J, cx);
     if constexpr (R == 1) ring_fill<32>(ring, cx.rs, cx.voff);
-    acs_segment<2, WEIGHTED, NM>(J, ring, cx, t0);
-    if constexpr (R == 2) acs_segment<3, WEIGHTED, NM>(J, ring, cx, t0);
+    acs_segment<2, WEIGHTED, NM>(J, ring, cx, t0, in);
+    if constexpr (R == 2) acs_segment<3, WEIGHTED, NM>(J, ring, cx, t0, in);
 }
 
 template <int P, int NM>
@@ -244,15 +265,22 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     round_write<1, 1>(J, cx);
     const int Q = n / 3;
     const int R = n % 3;
-    if (Q & 1) super_step<WEIGHTED, 1>(J, ring, cx, 0);
+    StepIn in = load_steps<WEIGHTED>(cx, 0);
+    if (Q & 1) {
+        StepIn next;
+        super_step<WEIGHTED, 1>(J, ring, cx, 0, in, next);
+        in = next;
+    }
     for (int q = Q & 1; q < Q; q += 2) {
-        super_step<WEIGHTED, 0>(J, ring, cx, 3 * q);
-        super_step<WEIGHTED, 1>(J, ring, cx, 3 * q + 3);
+        StepIn mid, next;
+        super_step<WEIGHTED, 0>(J, ring, cx, 3 * q, in, mid);
+        super_step<WEIGHTED, 1>(J, ring, cx, 3 * q + 3, mid, next);
+        in = next;
     }
     if (R == 1) {
-        tail_steps<WEIGHTED, 0, 1>(J, ring, cx, 3 * Q);
+        tail_steps<WEIGHTED, 0, 1>(J, ring, cx, 3 * Q, in);
     } else if (R == 2) {
-        tail_steps<WEIGHTED, 0, 2>(J, ring, cx, 3 * Q);
+        tail_steps<WEIGHTED, 0, 2>(J, ring, cx, 3 * Q, in);
     } else {
         __syncthreads();  // collect the last round
         round_read<1, 1>(J, cx);

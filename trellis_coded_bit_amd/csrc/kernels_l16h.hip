@@ -166,44 +166,111 @@ __device__ __forceinline__ void acsh_segment_impl(uint32_t (&J)[kRegs],
     cx.bpb.store(bp_word, acc);
 }
 
+// Weights and d of the full steps under the three half-steps of a super-step (index
+// P - 1; only the metric half-steps use them), held in scalar registers.  Requested one
+// super-step ahead so that they complete at a workgroup barrier: a wait for a scalar
+// load is also a wait for every LDS operation in flight.
+struct StepInH {
+    float w[3][2], d[3][2];
+};
+// Half-steps h0 .. h0 + 2; the full step of half-step h is h >> 1, clamped to the block.
+template <bool WEIGHTED, int V>
+__device__ __forceinline__ StepInH load_h(const CtxH &cx, int h0) {
+    StepInH s;
+    const int last = cx.nw / V - 1;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+        const int t = (h0 + p) >> 1 < last ? (h0 + p) >> 1 : last;
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            s.w[p][v] = v < V ? cx.wcol[t * V + v] : 0.0f;
+            s.d[p][v] = WEIGHTED && v < V ? cx.dcol[t * V + v] : 1.0f;
+        }
+    }
+    return s;
+}
+
 // Segment SEG of super-step q (half-steps 3q + 1 .. 3q + 3), pattern MP = q mod 2.
 template <int SEG, bool WEIGHTED, int NM, int V, int MP>
 __device__ __forceinline__ void acsh_segment(uint32_t (&J)[kRegs],
                                              float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
-                                             int h0) {
+                                             int h0, const StepInH &in) {
     constexpr int P = seg_step(SEG);
     const int h = h0 + P - 1;  // 0-based half-step index
-    float wt[2] = {0.0f, 0.0f}, dt[2] = {1.0f, 1.0f};
-    if constexpr (seg_has_metric(MP, SEG)) {
-        const int t = h >> 1;  // 0-based full step (h is odd here)
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-            wt[v] = cx.wcol[t * V + v];
-            if (WEIGHTED) dt[v] = cx.dcol[t * V + v];
-        }
-    }
-    acsh_segment_impl<SEG, WEIGHTED, NM, V, MP>(J, ring, cx, wt, dt,
+    acsh_segment_impl<SEG, WEIGHTED, NM, V, MP>(J, ring, cx, in.w[P - 1], in.d[P - 1],
                                                 2 * kThreads * h + seg_half(SEG),
                                                 std::make_integer_sequence<int, 16>{});
 }
 
-// Super-step under naming NM and pattern MP; entry and exit as in kernels_l16.hip.
+// Group I of segment SEG, with or without the metric as the pattern says.
+template <int SEG, bool WEIGHTED, int NM, int V, int MP, int I>
+__device__ __forceinline__ void acsh_group(uint32_t (&J)[kRegs], float4 (&ring)[Ring<V>::kSize],
+                                           const CtxH &cx, const StepInH &in, uint32_t &acc) {
+    constexpr int P = seg_step(SEG);
+    if constexpr (seg_has_metric(MP, SEG))
+        acsh_group_metric<SEG, WEIGHTED, NM, V, MP, I>(J, ring, cx.rs, cx.voff, in.w[P - 1],
+                                                       in.d[P - 1], acc);
+    else
+        acsh_group_plain<SEG, NM, I>(J, acc);
+}
+
+// Segment 2 (step 1 of the odd groups) with round 1 of the transposition read into the
+// registers it consumes, the four values of group i + 3 requested before group i (at
+// most 16 reads in flight; the LDS wait counter counts at most 15).
+template <bool WEIGHTED, int NM, int V, int MP, int I>
+__device__ __forceinline__ void seg2_group_h(uint32_t (&J)[kRegs],
+                                             float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
+                                             const StepInH &in, uint32_t &acc) {
+    if constexpr (I + 3 < 16) round_read_group<1 - NM, 1, I + 3>(J, cx);
+    acsh_group<2, WEIGHTED, NM, V, MP, I>(J, ring, cx, in, acc);
+}
+template <bool WEIGHTED, int NM, int V, int MP, int... I>
+__device__ __forceinline__ void seg2_reading_h(uint32_t (&J)[kRegs],
+                                               float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
+                                               int h0, const StepInH &in,
+                                               std::integer_sequence<int, I...>) {
+    round_read_groups<1 - NM, 1>(J, cx, std::make_integer_sequence<int, 3>{});
+    uint32_t acc = 0;
+    (seg2_group_h<WEIGHTED, NM, V, MP, I>(J, ring, cx, in, acc), ...);
+    cx.bpb.store(2 * kThreads * h0 + seg_half(2), acc);
+}
+
+// Groups I0 .. I0 + 7 of segment 5, their backpointer bits shifted into acc.
+template <bool WEIGHTED, int NM, int V, int MP, int I0, int... I>
+__device__ __forceinline__ void seg5_half_h(uint32_t (&J)[kRegs],
+                                            float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
+                                            const StepInH &in, uint32_t &acc,
+                                            std::integer_sequence<int, I...>) {
+    (acsh_group<5, WEIGHTED, NM, V, MP, I0 + I>(J, ring, cx, in, acc), ...);
+}
+
+// Super-step under naming NM and pattern MP, with the weights of its half-steps in `in`
+// and those of the next super-step requested into `next`; entry and exit as in
+// kernels_l16.hip.
 template <bool WEIGHTED, int NM, int V, int MP>
 __device__ __forceinline__ void super_step_h(uint32_t (&J)[kRegs],
                                              float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
-                                             int h0) {
-    acsh_segment<0, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
-    acsh_segment<1, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
+                                             int h0, const StepInH &in, StepInH &next) {
+    acsh_segment<0, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in);
+    acsh_segment<1, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in);
     __syncthreads();  // round-1 values written by every wave
-    round_read<1 - NM, 1>(J, cx);
-    acsh_segment<2, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
-    acsh_segment<3, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
-    acsh_segment<4, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
+    seg2_reading_h<WEIGHTED, NM, V, MP>(J, ring, cx, h0, in,
+                                        std::make_integer_sequence<int, 16>{});
+    acsh_segment<3, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in);
+    acsh_segment<4, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in);
     __syncthreads();  // every wave has read round 1
     round_write<NM, 0>(J, cx);
-    acsh_segment<5, WEIGHTED, NM, V, MP>(J, ring, cx, h0);
+    // segment 5 works on the r[6] = 1 registers only, so its second half runs while the
+    // round-0 values (which refill the r[6] = 0 registers) are on their way in
+    uint32_t acc5 = 0;
+    seg5_half_h<WEIGHTED, NM, V, MP, 0>(J, ring, cx, in, acc5,
+                                        std::make_integer_sequence<int, 8>{});
+    next = load_h<WEIGHTED, V>(cx, h0 + 3);
     __syncthreads();  // round-0 values written by every wave
     round_read<NM, 0>(J, cx);
+    seg5_half_h<WEIGHTED, NM, V, MP, 8>(J, ring, cx, in, acc5,
+                                        std::make_integer_sequence<int, 8>{});
+    cx.bpb.store(2 * kThreads * (h0 + 2) + seg_half(5), acc5);
     __syncthreads();  // every wave has read round 0
     round_write<NM, 1>(J, cx);
 }
@@ -213,13 +280,13 @@ __device__ __forceinline__ void super_step_h(uint32_t (&J)[kRegs],
 // no refill.
 template <bool WEIGHTED, int V, int MP, int R>
 __device__ __forceinline__ void tail_h(uint32_t (&J)[kRegs], float4 (&ring)[Ring<V>::kSize],
-                                       const CtxH &cx, int h0) {
-    acsh_segment<0, WEIGHTED, 0, V, MP>(J, ring, cx, h0);
-    if constexpr (R == 2) acsh_segment<1, WEIGHTED, 0, V, MP>(J, ring, cx, h0);
+                                       const CtxH &cx, int h0, const StepInH &in) {
+    acsh_segment<0, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
+    if constexpr (R == 2) acsh_segment<1, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
     __syncthreads();
     round_read<1, 1>(J, cx);
-    acsh_segment<2, WEIGHTED, 0, V, MP>(J, ring, cx, h0);
-    if constexpr (R == 2) acsh_segment<3, WEIGHTED, 0, V, MP>(J, ring, cx, h0);
+    acsh_segment<2, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
+    if constexpr (R == 2) acsh_segment<3, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
 }
 
 template <int P, int NM>
@@ -268,25 +335,32 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
     const int nh = 2 * n;
     const int Q = nh / 3;
     const int R = nh % 3;
+    StepInH in = load_h<WEIGHTED, V>(cx, 0);
     if (Q & 1) {
-        super_step_h<WEIGHTED, 1, V, 0>(J, ring, cx, 0);
+        StepInH next;
+        super_step_h<WEIGHTED, 1, V, 0>(J, ring, cx, 0, in, next);
+        in = next;
         for (int q = 1; q < Q; q += 2) {
-            super_step_h<WEIGHTED, 0, V, 1>(J, ring, cx, 3 * q);
-            super_step_h<WEIGHTED, 1, V, 0>(J, ring, cx, 3 * q + 3);
+            StepInH mid, nx;
+            super_step_h<WEIGHTED, 0, V, 1>(J, ring, cx, 3 * q, in, mid);
+            super_step_h<WEIGHTED, 1, V, 0>(J, ring, cx, 3 * q + 3, mid, nx);
+            in = nx;
         }
     } else {
         for (int q = 0; q < Q; q += 2) {
-            super_step_h<WEIGHTED, 0, V, 0>(J, ring, cx, 3 * q);
-            super_step_h<WEIGHTED, 1, V, 1>(J, ring, cx, 3 * q + 3);
+            StepInH mid, nx;
+            super_step_h<WEIGHTED, 0, V, 0>(J, ring, cx, 3 * q, in, mid);
+            super_step_h<WEIGHTED, 1, V, 1>(J, ring, cx, 3 * q + 3, mid, nx);
+            in = nx;
         }
     }
     // the tail is super-step Q, pattern Q mod 2
     if (R == 1) {
-        if (Q & 1) tail_h<WEIGHTED, V, 1, 1>(J, ring, cx, 3 * Q);
-        else tail_h<WEIGHTED, V, 0, 1>(J, ring, cx, 3 * Q);
+        if (Q & 1) tail_h<WEIGHTED, V, 1, 1>(J, ring, cx, 3 * Q, in);
+        else tail_h<WEIGHTED, V, 0, 1>(J, ring, cx, 3 * Q, in);
     } else if (R == 2) {
-        if (Q & 1) tail_h<WEIGHTED, V, 1, 2>(J, ring, cx, 3 * Q);
-        else tail_h<WEIGHTED, V, 0, 2>(J, ring, cx, 3 * Q);
+        if (Q & 1) tail_h<WEIGHTED, V, 1, 2>(J, ring, cx, 3 * Q, in);
+        else tail_h<WEIGHTED, V, 0, 2>(J, ring, cx, 3 * Q, in);
     } else {
         __syncthreads();
         round_read<1, 1>(J, cx);

@@ -134,29 +134,79 @@ __device__ __forceinline__ void acs3_segment_impl(uint32_t (&J)[kRegs],
 
 template <int SEG, bool WEIGHTED, int NM>
 __device__ __forceinline__ void acs3_segment(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch3],
-                                             const Ctx &cx, int t0) {
+                                             const Ctx &cx, int t0, const StepIn &in) {
     constexpr int P = seg3_step(SEG);
     const int t = t0 + P - 1;
-    acs3_segment_impl<SEG, WEIGHTED, NM>(J, ring, cx.rs, cx.voff, cx.wcol[t],
-                                         WEIGHTED ? cx.dcol[t] : 1.0f,
+    acs3_segment_impl<SEG, WEIGHTED, NM>(J, ring, cx.rs, cx.voff, in.w[P - 1], in.d[P - 1],
                                          cx.bp + 2 * kThreads * t + seg3_half(SEG),
                                          std::make_integer_sequence<int, 8>{});
 }
 
-// Super-step (steps t0+1, t0+2) under naming NM; entry and exit as in kernels_l16.hip.
+// The eight registers of step-1 group g = 2 I + RHO (the registers segment RHO of a
+// super-step consumes together), read from transposition round RHO.
+template <int NM, int RHO, int I>
+__device__ __forceinline__ void round_read_group3(uint32_t (&J)[kRegs], const Ctx &cx) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        constexpr uint32_t g = 2u * I + RHO;
+        const uint32_t r = group_reg3(1, g, b);
+        const uint32_t off = 4u * lds_read_reg(r);
+        const uint32_t k = off / (4u * 2112u * 4u);
+        J[phys(1 - NM, r)] = lds_get(cx.rb[k], off - k * 4u * 2112u * 4u);
+    }
+}
+
+// Segment 1 (step 1 of the odd groups) with round 1 of the transposition read into the
+// registers it consumes: the eight values of group i + 1 are requested before group i
+// is computed, so at most 16 reads are in flight (the LDS wait counter counts at most
+// 15) and each group waits only for its own values.
+template <bool WEIGHTED, int NM, int I>
+__device__ __forceinline__ void seg1_group3(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch3],
+                                            const Ctx &cx, float wt, float dt, uint32_t &acc) {
+    if constexpr (I + 1 < 8) round_read_group3<1 - NM, 1, I + 1>(J, cx);
+    acs3_group<1, WEIGHTED, NM, I>(J, ring, cx.rs, cx.voff, wt, dt, acc);
+}
+template <bool WEIGHTED, int NM, int... I>
+__device__ __forceinline__ void seg1_reading3(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch3],
+                                              const Ctx &cx, int t0, const StepIn &in,
+                                              std::integer_sequence<int, I...>) {
+    round_read_group3<1 - NM, 1, 0>(J, cx);
+    uint32_t acc = 0;
+    (seg1_group3<WEIGHTED, NM, I>(J, ring, cx, in.w[0], in.d[0], acc), ...);
+    cx.bp[2 * kThreads * t0 + seg3_half(1)] = acc;
+}
+
+// Groups I0 .. I0 + 3 of segment 3, their backpointer bits shifted into acc.
+template <bool WEIGHTED, int NM, int I0, int... I>
+__device__ __forceinline__ void seg3_quarter(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch3],
+                                             const Ctx &cx, const StepIn &in, uint32_t &acc,
+                                             std::integer_sequence<int, I...>) {
+    (acs3_group<3, WEIGHTED, NM, I0 + I>(J, ring, cx.rs, cx.voff, in.w[1], in.d[1], acc), ...);
+}
+
+// Super-step (steps t0+1, t0+2) under naming NM, with the weights (and d) of its two
+// steps in `in`; those of the next super-step are requested into `next` and complete at
+// a barrier (a wait for a scalar load would also wait for every LDS operation in flight).
+// Entry and exit as in kernels_l16.hip.
 template <bool WEIGHTED, int NM>
 __device__ __forceinline__ void super_step3(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch3],
-                                            const Ctx &cx, int t0) {
-    acs3_segment<0, WEIGHTED, NM>(J, ring, cx, t0);
+                                            const Ctx &cx, int t0, const StepIn &in,
+                                            StepIn &next) {
+    acs3_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
     __syncthreads();  // round-1 values written by every wave
-    round_read<1 - NM, 1>(J, cx);
-    acs3_segment<1, WEIGHTED, NM>(J, ring, cx, t0);
-    acs3_segment<2, WEIGHTED, NM>(J, ring, cx, t0);
+    seg1_reading3<WEIGHTED, NM>(J, ring, cx, t0, in, std::make_integer_sequence<int, 8>{});
+    acs3_segment<2, WEIGHTED, NM>(J, ring, cx, t0, in);
     __syncthreads();  // every wave has read round 1
     round_write<NM, 0>(J, cx);
-    acs3_segment<3, WEIGHTED, NM>(J, ring, cx, t0);
+    // segment 3 works on the r[6] = 1 registers only, so its second half runs while the
+    // round-0 values (which refill the r[6] = 0 registers) are on their way in
+    uint32_t acc3 = 0;
+    seg3_quarter<WEIGHTED, NM, 0>(J, ring, cx, in, acc3, std::make_integer_sequence<int, 4>{});
+    next = load_steps<WEIGHTED>(cx, t0 + 2);
     __syncthreads();  // round-0 values written by every wave
     round_read<NM, 0>(J, cx);
+    seg3_quarter<WEIGHTED, NM, 4>(J, ring, cx, in, acc3, std::make_integer_sequence<int, 4>{});
+    cx.bp[2 * kThreads * (t0 + 1) + seg3_half(3)] = acc3;
     __syncthreads();  // every wave has read round 0
     round_write<NM, 1>(J, cx);
 }
@@ -202,16 +252,23 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16k3_kernel(
 
     const int Q = n / 2;
     const int R = n % 2;
-    if (Q & 1) super_step3<WEIGHTED, 1>(J, ring, cx, 0);
+    StepIn in = load_steps<WEIGHTED>(cx, 0);
+    if (Q & 1) {
+        StepIn next;
+        super_step3<WEIGHTED, 1>(J, ring, cx, 0, in, next);
+        in = next;
+    }
     for (int q = Q & 1; q < Q; q += 2) {
-        super_step3<WEIGHTED, 0>(J, ring, cx, 2 * q);
-        super_step3<WEIGHTED, 1>(J, ring, cx, 2 * q + 2);
+        StepIn mid, next;
+        super_step3<WEIGHTED, 0>(J, ring, cx, 2 * q, in, mid);
+        super_step3<WEIGHTED, 1>(J, ring, cx, 2 * q + 2, mid, next);
+        in = next;
     }
     if (R == 1) {  // one more step: segments 0 and 1 under naming 0
-        acs3_segment<0, WEIGHTED, 0>(J, ring, cx, 2 * Q);
+        acs3_segment<0, WEIGHTED, 0>(J, ring, cx, 2 * Q, in);
         __syncthreads();
         round_read<1, 1>(J, cx);
-        acs3_segment<1, WEIGHTED, 0>(J, ring, cx, 2 * Q);
+        acs3_segment<1, WEIGHTED, 0>(J, ring, cx, 2 * Q, in);
     } else {
         __syncthreads();
         round_read<1, 1>(J, cx);

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <utility>
 
 #include "l16_layout.h"
 
@@ -47,6 +48,7 @@ struct Ctx {
     const float *wcol;          // the block's T weights
     const float *dcol;          // the block's T values of d (weighted only)
     uint32_t *bp;               // lane's backpointer words: + 2 * kThreads * t + half
+    int nw;                     // weights in the block
     uint32_t wb[2];             // LDS byte bases for round writes
     uint32_t rb[4];             // LDS byte bases for round reads
 };
@@ -62,6 +64,7 @@ __device__ __forceinline__ Ctx make_ctx(const float *W, int64_t ldw, const float
     Ctx cx;
     const uint32_t wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform
     cx.wcol = W + row * ldw + col * n;
+    cx.nw = n;
     // the offset, not the pointer, is selected: d keeps its provenance, so its per-step
     // values are read with scalar loads (a vector load's wait would drain the codebook
     // loads in flight)
@@ -110,6 +113,28 @@ __device__ __forceinline__ BpBuf make_bpbuf(uint2 *bp_block, int64_t bp_per_bloc
     return b;
 }
 
+// Weight and d of the three steps of a super-step, held in scalar registers.  They are
+// requested one super-step ahead and complete at a workgroup barrier (which waits for
+// every LDS and scalar-memory operation), so their use needs no wait: a wait for a
+// scalar load is a wait for every LDS operation in flight, which would serialise the
+// transposition rounds.
+struct StepIn {
+    float w[3], d[3];
+};
+// Steps t0 .. t0 + 2 of a block with one weight per step, each index clamped to the
+// block's last weight (past the end the values are never used).
+template <bool WEIGHTED>
+__device__ __forceinline__ StepIn load_steps(const Ctx &cx, int t0) {
+    StepIn s;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+        const int t = t0 + p < cx.nw ? t0 + p : cx.nw - 1;
+        s.w[p] = cx.wcol[t];
+        s.d[p] = WEIGHTED ? cx.dcol[t] : 1.0f;
+    }
+    return s;
+}
+
 extern __shared__ uint32_t lds_stage[];
 
 __device__ __forceinline__ void lds_put(uint32_t base, uint32_t off, uint32_t v) {
@@ -132,15 +157,28 @@ __device__ __forceinline__ void round_write(const uint32_t (&J)[kRegs], const Ct
         lds_put(cx.wb[bit(r, 4)], off - bit(r, 4) * 4u * 2112u * 8u, J[phys(NM, r)]);
     }
 }
-template <int NM, int RHO>
-__device__ __forceinline__ void round_read(uint32_t (&J)[kRegs], const Ctx &cx) {
+// The four registers of group g = 2 i + RHO at step 1 (the registers the next segment
+// that needs round RHO consumes together).
+template <int NM, int RHO, int I>
+__device__ __forceinline__ void round_read_group(uint32_t (&J)[kRegs], const Ctx &cx) {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-        const uint32_t r = 2u * i + RHO;
+    for (int b = 0; b < 4; ++b) {
+        constexpr uint32_t g = 2u * I + RHO;
+        const uint32_t r = group_reg(1, g, b);
         const uint32_t off = 4u * lds_read_reg(r);
         const uint32_t k = off / (4u * 2112u * 4u);
         J[phys(1 - NM, r)] = lds_get(cx.rb[k], off - k * 4u * 2112u * 4u);
     }
+}
+template <int NM, int RHO, int... I>
+__device__ __forceinline__ void round_read_groups(uint32_t (&J)[kRegs], const Ctx &cx,
+                                                  std::integer_sequence<int, I...>) {
+    (round_read_group<NM, RHO, I>(J, cx), ...);
+}
+// All 64 registers r[0] = RHO, group by group.
+template <int NM, int RHO>
+__device__ __forceinline__ void round_read(uint32_t (&J)[kRegs], const Ctx &cx) {
+    round_read_groups<NM, RHO>(J, cx, std::make_integer_sequence<int, 16>{});
 }
 
 // Lowest-index minimum over the workgroup: (bv, bi) are each lane's best cost pattern
