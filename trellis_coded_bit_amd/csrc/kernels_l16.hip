@@ -295,8 +295,23 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     block_select(bv, bi, w, l, send + blockIdx.x, cost_out + blk);
 }
 
+// Remembered predecessor index j of state s at step t (1-based): s_{t-1} = (j << 14) |
+// (s >> 2).
+__device__ __forceinline__ uint32_t bp_choice(const uint2 *bpb, int t, uint32_t s) {
+    const int p = (t - 1) % 3 + 1;
+    const Slot sl = slot_of(p, s);
+    const uint32_t g = reg_group(p, sl.r);
+    const uint2 word = bpb[(t - 1) * kThreads + sl.w * kLanes + sl.l];
+    const uint32_t bits = bp_half(p, g) ? word.y : word.x;
+    return (bits >> bp_shift(p, g)) & 3u;
+}
+
 // One wave per block: follow the remembered predecessors back from the end state and
-// pack the 2-bit chunks b_1..b_n, MSB first, into MSB-first words.
+// pack the 2-bit chunks b_1..b_n, MSB first, into MSB-first words.  Three steps per
+// memory round trip: with s_t known, lane 0 reads the choice at step t for s_t, lanes
+// 1..4 the choice at step t-1 for each of the four possible s_{t-1}, and lanes 5..20
+// the choice at step t-2 for each of the sixteen possible s_{t-2}; the three reads are
+// independent, and the wave then picks the path they determine.
 __global__ __launch_bounds__(64) void traceback_l16_kernel(
     const uint2 *__restrict__ bp, int64_t bp_per_block, const uint32_t *__restrict__ send,
     int n, int nwords, int64_t block0, uint32_t *__restrict__ bitstream,
@@ -305,20 +320,48 @@ __global__ __launch_bounds__(64) void traceback_l16_kernel(
     const int lane = threadIdx.x;
     const uint2 *bpb = bp + blockIdx.x * bp_per_block;
     const int64_t blk = block0 + blockIdx.x;
-    if (lane == 0) {
-        uint32_t s = send[blockIdx.x];
-        for (int t = n; t >= 1; --t) {
-            const int p = (t - 1) % 3 + 1;
-            const Slot sl = slot_of(p, s);
-            const uint32_t g = reg_group(p, sl.r);
-            const uint2 word = bpb[(t - 1) * kThreads + sl.w * kLanes + sl.l];
-            const uint32_t bits = bp_half(p, g) ? word.y : word.x;
-            const uint32_t jb = (bits >> bp_shift(p, g)) & 3u;
-            chunk[t - 1] = static_cast<uint8_t>(s & 3u);
-            s = (jb << 14) | (s >> 2);
+    uint32_t s = send[blockIdx.x];  // s_t, the same in every lane
+    int t = n;
+    while (t >= 1) {
+        // this lane's candidate: level 0 is s_t itself, level 1 s_{t-1} = (j0 << 14) |
+        // (s_t >> 2), level 2 s_{t-2} = (j1 << 14) | (s_{t-1} >> 2)
+        int lvl = -1;
+        uint32_t c = 0;
+        if (lane == 0) {
+            lvl = 0;
+            c = s;
+        } else if (lane < 5) {
+            lvl = 1;
+            c = (static_cast<uint32_t>(lane - 1) << 14) | (s >> 2);
+        } else if (lane < 21) {
+            lvl = 2;
+            const uint32_t j0 = static_cast<uint32_t>(lane - 5) >> 2;
+            const uint32_t j1 = static_cast<uint32_t>(lane - 5) & 3u;
+            c = (j1 << 14) | (((j0 << 14) | (s >> 2)) >> 2);
         }
-        start_state[blk] = s;
+        uint32_t jb = 0;
+        if (lvl >= 0 && t - lvl >= 1) jb = bp_choice(bpb, t - lvl, c);
+        const uint32_t j0 = __builtin_amdgcn_readlane(jb, 0);
+        if (lane == 0) chunk[t - 1] = static_cast<uint8_t>(s & 3u);
+        const uint32_t s1 = (j0 << 14) | (s >> 2);
+        if (t == 1) {
+            s = s1;
+            break;
+        }
+        const uint32_t j1 = __builtin_amdgcn_readlane(jb, 1 + static_cast<int>(j0));
+        if (lane == 0) chunk[t - 2] = static_cast<uint8_t>(s1 & 3u);
+        const uint32_t s2 = (j1 << 14) | (s1 >> 2);
+        if (t == 2) {
+            s = s2;
+            break;
+        }
+        const uint32_t j2 =
+            __builtin_amdgcn_readlane(jb, 5 + 4 * static_cast<int>(j0) + static_cast<int>(j1));
+        if (lane == 0) chunk[t - 3] = static_cast<uint8_t>(s2 & 3u);
+        s = (j2 << 14) | (s2 >> 2);
+        t -= 3;
     }
+    if (lane == 0) start_state[blk] = s;
     __syncthreads();
     for (int wi = lane; wi < nwords; wi += 64) {
         uint32_t word = 0;

@@ -293,20 +293,44 @@ __global__ __launch_bounds__(64) void traceback_l16k3_kernel(
     const int lane = threadIdx.x;
     const uint2 *bpb = bp + blockIdx.x * bp_per_block;
     const int64_t blk = block0 + blockIdx.x;
-    if (lane == 0) {
-        uint32_t s = send[blockIdx.x];
-        for (int t = n; t >= 1; --t) {
-            const int p = (t - 1) % 2 + 1;
-            const Slot sl = slot_of3(p, s);
-            const uint32_t g = reg_group3(p, sl.r);
-            const uint2 word = bpb[(t - 1) * kThreads + sl.w * kLanes + sl.l];
-            const uint32_t bits = bp3_half(p, g) ? word.y : word.x;
-            const uint32_t jb = (bits >> bp3_shift(p, g)) & 7u;
-            chunk[t - 1] = static_cast<uint8_t>(s & 7u);
-            s = (jb << 13) | (s >> 3);
+    // Two steps per memory round trip: with s_t known, lane 0 reads the choice at step t
+    // for s_t and lanes 1..8 the choice at step t-1 for each of the eight possible
+    // s_{t-1} = (j << 13) | (s_t >> 3); the wave then picks the path they determine.
+    uint32_t s = send[blockIdx.x];  // s_t, the same in every lane
+    int t = n;
+    while (t >= 1) {
+        int lvl = -1;
+        uint32_t c = 0;
+        if (lane == 0) {
+            lvl = 0;
+            c = s;
+        } else if (lane < 9) {
+            lvl = 1;
+            c = (static_cast<uint32_t>(lane - 1) << 13) | (s >> 3);
         }
-        start_state[blk] = s;
+        uint32_t jb = 0;
+        if (lvl >= 0 && t - lvl >= 1) {
+            const int tt = t - lvl;
+            const int p = (tt - 1) % 2 + 1;
+            const Slot sl = slot_of3(p, c);
+            const uint32_t g = reg_group3(p, sl.r);
+            const uint2 word = bpb[(tt - 1) * kThreads + sl.w * kLanes + sl.l];
+            const uint32_t bits = bp3_half(p, g) ? word.y : word.x;
+            jb = (bits >> bp3_shift(p, g)) & 7u;
+        }
+        const uint32_t j0 = __builtin_amdgcn_readlane(jb, 0);
+        if (lane == 0) chunk[t - 1] = static_cast<uint8_t>(s & 7u);
+        const uint32_t s1 = (j0 << 13) | (s >> 3);
+        if (t == 1) {
+            s = s1;
+            break;
+        }
+        const uint32_t j1 = __builtin_amdgcn_readlane(jb, 1 + static_cast<int>(j0));
+        if (lane == 0) chunk[t - 2] = static_cast<uint8_t>(s1 & 7u);
+        s = (j1 << 13) | (s1 >> 3);
+        t -= 2;
     }
+    if (lane == 0) start_state[blk] = s;
     __syncthreads();
     const int total = 3 * n;
     for (int wi = lane; wi < nwords; wi += 64) {
