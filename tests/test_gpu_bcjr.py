@@ -75,6 +75,7 @@ CASES = [
     (16, 3, 1, 256, 1, 256, True),
     (16, 2, 2, 256, 1, 256, False),
     (16, 1, 1, 40, 1, 80, True),
+    (16, 2, 1, 1024, 1, 1024, False),  # longest block: 1024 steps, 64 MiB of stored vectors
 ]
 
 

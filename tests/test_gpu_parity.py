@@ -74,7 +74,9 @@ L16_EDGES = [(16, 2, 1, n, 2, 2 * n, n % 2 == 0) for n in range(1, 13)] + \
             [(16, 2, 2, 2 * n, 2, 4 * n, n % 2 == 1) for n in range(1, 13)] + \
             [(16, 4, 1, n, 2, 2 * n, n % 2 == 0) for n in range(1, 9)] + \
             [(16, 2, 2, 256, 2, 512, True), (16, 2, 2, 254, 1, 508, False),
-             (16, 4, 1, 256, 1, 512, True)]
+             (16, 4, 1, 256, 1, 512, True)] + \
+            [(16, 2, 1, 1024, 1, 1024, True), (16, 2, 1, 1022, 1, 1022, False),
+             (16, 3, 1, 1024, 1, 1024, True), (16, 2, 2, 1024, 1, 1024, False)]  # longest blocks
 
 
 @pytest.mark.parametrize("L,k,V,T,M,N,weighted", SMALL + L16_EDGES)
