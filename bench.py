@@ -25,12 +25,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "weights encoded/s (L=16,k=2,T=256 Viterbi) + % VALU peak ACS ops/s"
 
-# MI355X: 256 compute units, 4 SIMDs x 16 lanes each (64 fp32 VALU lane-ops per clock
-# per CU, non-packed), 2.4 GHz peak engine clock.
+# MI355X: 256 compute units of 4 SIMDs, 2.4 GHz peak engine clock.  A SIMD issues up to
+# two wave64 VALU instructions (from different waves) every 4 clocks: 128 VALU lane-ops
+# per clock per CU, non-packed.  This is the published fp32 vector rate (157.3 TFLOP/s)
+# with an FMA counted as one op instead of two.  (Not every instruction pairs: v_min3 and
+# other 3-source integer ops issue one per 4 clocks.)
 N_CU = 256
-LANES_PER_CU_CLK = 64
+LANES_PER_CU_CLK = 128
 CLOCK_HZ = 2.4e9
-VALU_PEAK_OPS = N_CU * LANES_PER_CU_CLK * CLOCK_HZ  # 3.93e13 lane-ops/s
+VALU_PEAK_OPS = N_CU * LANES_PER_CU_CLK * CLOCK_HZ  # 7.86e13 lane-ops/s
 HBM_PEAK_GBPS = 8000.0
 
 
