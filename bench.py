@@ -364,6 +364,11 @@ def main():
     peak_tops = VALU_PEAK_OPS / 1e12
     bp_bytes = nb * (w.T // w.V) * (1 << (w.L - w.k * w.V)) * (w.k * w.V) / 8
     bp_gbps = bp_bytes / (acs_ms / 1e3) / 1e9
+    # Every state update reads its successor's V codebook values (fp32) from L2: the
+    # register-resident forward kernels stream 4 V bytes per update from the L2-resident
+    # codebook copies, and this stream, not HBM, is what bounds them in practice.
+    cb_bytes = updates_per_launch * 4 * w.V
+    cb_b_per_clk_cu = cb_bytes / (acs_ms / 1e3) / (N_CU * CLOCK_HZ)
 
     result = {
         "metric": METRIC,
@@ -387,6 +392,7 @@ def main():
         "acs": {"kernel_ms": acs_ms, "state_updates_per_s": acs_ops_per_s,
                 "valu_ops_per_update": ops, "valu_pct": 100.0 * achieved_tops / peak_tops,
                 "bp_write_GBps": bp_gbps, "bp_pct_hbm": 100.0 * bp_gbps / HBM_PEAK_GBPS,
+                "codebook_l2_bytes": cb_bytes, "codebook_l2_B_per_clk_per_cu": cb_b_per_clk_cu,
                 "share_of_step": acs_ms / ms_per_step},
     }
     if args.gemv_iters > 0:
