@@ -64,6 +64,26 @@ def test_hadamard_parity(oracle_lib, n, rows, chunks):
     assert np.allclose(Yi.cpu().numpy(), X, atol=1e-5)
 
 
+@pytest.mark.parametrize("n", [256, 2048])
+def test_hadamard_unaligned_rows(oracle_lib, n):
+    """Rows that start 4 bytes past a 16-byte boundary (a column-offset view, odd row
+    stride) take the 4-byte-access kernel; aligned rows take the 16-byte one."""
+    import oracle
+    _say(f"hadamard unaligned n={n}")
+    rng = np.random.default_rng(7 * n)
+    rows, length = 3, 2 * n
+    base = rng.standard_normal((rows, length + 1)).astype(np.float32)
+    sigma = rng.choice([-1.0, 1.0], size=length).astype(np.float32)
+    Bt = torch.from_numpy(base).cuda()
+    Xv = Bt[:, 1:]
+    assert Xv.data_ptr() % 16 != 0 and Xv.stride(0) % 4 != 0
+    Y = api.hadamard(Xv, n, torch.from_numpy(sigma).cuda())
+    torch.cuda.synchronize()
+    X = base[:, 1:]
+    ref = oracle.hadamard(np.ascontiguousarray(X), n, sigma.astype(np.float64))
+    assert np.all(np.abs(Y.cpu().numpy() - ref) <= _had_tol(X, n))
+
+
 def test_hadamard_page_example_and_in_place(oracle_lib):
     x = torch.tensor([[3.0, 0.2, -0.1, 0.1]], device="cuda")
     api.hadamard(x, 4, out=x)                    # in place, no signs

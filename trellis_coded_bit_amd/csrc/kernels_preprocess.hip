@@ -74,6 +74,90 @@ __global__ __launch_bounds__(256) void fwht_wave_kernel(
     }
 }
 
+// Chunks of n = 256 F values with 16-byte aligned rows: one wave per chunk, element
+// i = q + 4 lane + 256 j in component q of float4 register j.  Index bits 0, 1 are
+// butterflies inside a float4, bits 2..7 go through cross-lane shuffles, bits 8.. are
+// butterflies between registers; each load or store moves 1 KiB per wave.  The levels
+// commute, so the order differs from fwht_wave_kernel only in rounding.
+template <int F>
+__global__ __launch_bounds__(256) void fwht_wave4_kernel(
+    const float *__restrict__ X, int64_t ldx, float *__restrict__ Y, int64_t ldy,
+    int64_t rows, int64_t chunks_per_row, const float *__restrict__ sigma, int inverse,
+    float scale) {
+    constexpr int n = 256 * F;
+    const int lane = threadIdx.x & 63;
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (chunk >= rows * chunks_per_row) return;
+    const int64_t r = chunk / chunks_per_row;
+    const int64_t c0 = (chunk % chunks_per_row) * n;
+    const float4 *x = reinterpret_cast<const float4 *>(X + r * ldx + c0);
+    const float4 *sg = sigma ? reinterpret_cast<const float4 *>(sigma + c0) : nullptr;
+    float v[F][4];
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+        float4 t = x[j * 64 + lane];
+        if (sg && !inverse) {
+            const float4 g = sg[j * 64 + lane];
+            t.x *= g.x;
+            t.y *= g.y;
+            t.z *= g.z;
+            t.w *= g.w;
+        }
+        v[j][0] = t.x;
+        v[j][1] = t.y;
+        v[j][2] = t.z;
+        v[j][3] = t.w;
+    }
+    // index bits 0 and 1 (inside the float4)
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+        const float a0 = v[j][0] + v[j][1], a1 = v[j][0] - v[j][1];
+        const float a2 = v[j][2] + v[j][3], a3 = v[j][2] - v[j][3];
+        v[j][0] = a0 + a2;
+        v[j][2] = a0 - a2;
+        v[j][1] = a1 + a3;
+        v[j][3] = a1 - a3;
+    }
+    // index bits 2..7 (lanes)
+#pragma unroll
+    for (int p = 1; p < 64; p <<= 1) {
+        const bool upper = (lane & p) != 0;
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float o = __shfl_xor(v[j][q], p);
+                v[j][q] = upper ? o - v[j][q] : v[j][q] + o;
+            }
+    }
+    // index bits 8.. (registers)
+#pragma unroll
+    for (int h = 1; h < F; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+            if ((j & h) == 0)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float a = v[j][q], b = v[j + h][q];
+                    v[j][q] = a + b;
+                    v[j + h][q] = a - b;
+                }
+    float4 *y = reinterpret_cast<float4 *>(Y + r * ldy + c0);
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+        float4 t = make_float4(v[j][0] * scale, v[j][1] * scale, v[j][2] * scale,
+                               v[j][3] * scale);
+        if (sg && inverse) {
+            const float4 g = sg[j * 64 + lane];
+            t.x *= g.x;
+            t.y *= g.y;
+            t.z *= g.z;
+            t.w *= g.w;
+        }
+        y[j * 64 + lane] = t;
+    }
+}
+
 // Small chunks (n < 64): one workgroup of 64 threads per row, the row staged in LDS and
 // one barrier per butterfly level.
 __global__ __launch_bounds__(64) void fwht_small_kernel(
@@ -131,15 +215,16 @@ __global__ __launch_bounds__(256) void col_partial_kernel(
     if (c >= N) return;
     const int64_t r0 = static_cast<int64_t>(blockIdx.y) * slab_rows;
     const int64_t r1 = (r0 + slab_rows < M) ? r0 + slab_rows : M;
-    // rows in ascending order; loads of 8 rows are issued before their sums
+    // rows in ascending order; loads of 32 rows are issued before their sums (the walk
+    // is a chain of dependent sums, so the loads are what it waits for)
     float s = 0.0f;
     int64_t r = r0;
-    for (; r + 8 <= r1; r += 8) {
-        float v[8];
+    for (; r + 32 <= r1; r += 32) {
+        float v[32];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = W[(r + i) * ldw + c] / a[r + i];
+        for (int i = 0; i < 32; ++i) v[i] = W[(r + i) * ldw + c] / a[r + i];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s = __builtin_fmaf(v[i], v[i], s);
+        for (int i = 0; i < 32; ++i) s = __builtin_fmaf(v[i], v[i], s);
     }
     for (; r < r1; ++r) {
         const float v = W[r * ldw + c] / a[r];
@@ -153,15 +238,16 @@ __global__ __launch_bounds__(256) void col_finalize_kernel(const float *__restri
                                                            float *__restrict__ b) {
     const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (c >= N) return;
-    // slab sums in ascending order; loads of 8 slabs are issued before their sums
+    // slab sums in ascending order; the loads of all (up to 64) slabs are issued before
+    // their sums
     float s = 0.0f;
     int i = 0;
-    for (; i + 8 <= nslabs; i += 8) {
-        float v[8];
+    for (; i + 64 <= nslabs; i += 64) {
+        float v[64];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = part[static_cast<int64_t>(i + q) * N + c];
+        for (int q = 0; q < 64; ++q) v[q] = part[static_cast<int64_t>(i + q) * N + c];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) s += v[q];
+        for (int q = 0; q < 64; ++q) s += v[q];
     }
     for (; i < nslabs; ++i) s += part[static_cast<int64_t>(i) * N + c];
     b[c] = s > 0.0f ? __builtin_sqrtf(s / static_cast<float>(M)) : 1.0f;
@@ -175,6 +261,17 @@ __global__ __launch_bounds__(256) void scale_apply_kernel(
     for (int64_t c = static_cast<int64_t>(blockIdx.y) * 256 + threadIdx.x; c < N;
          c += static_cast<int64_t>(gridDim.y) * 256)
         Wn[r * ldn + c] = W[r * ldw + c] / (ar * b[c]);
+}
+
+template <int F>
+hipError_t launch_wave4(const float *X, int64_t ldx, float *Y, int64_t ldy, int64_t rows,
+                        int64_t cpr, const float *sigma, int inverse, float scale,
+                        hipStream_t s) {
+    const int64_t chunks = rows * cpr;
+    const int64_t grid = (chunks + 3) / 4;
+    hipLaunchKernelGGL(fwht_wave4_kernel<F>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                       s, X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale);
+    return hipGetLastError();
 }
 
 template <int E>
@@ -197,6 +294,20 @@ hipError_t launch_hadamard(const float *X, int64_t ldx, float *Y, int64_t ldy, i
                            hipStream_t s) {
     const float scale = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(n)));
     const int64_t cpr = len / n;
+    // 16-byte rows (and signs): float4 loads and stores
+    const bool a16 = ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(Y) |
+                       reinterpret_cast<uintptr_t>(sigma)) & 15u) == 0 &&
+                     ldx % 4 == 0 && ldy % 4 == 0;
+    if (a16) {
+        switch (n) {
+            case 256: return launch_wave4<1>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+            case 512: return launch_wave4<2>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+            case 1024: return launch_wave4<4>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+            case 2048: return launch_wave4<8>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+            case 4096: return launch_wave4<16>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
+            default: break;
+        }
+    }
     switch (n) {
         case 64: return launch_wave<1>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
         case 128: return launch_wave<2>(X, ldx, Y, ldy, rows, cpr, sigma, inverse, scale, s);
