@@ -119,6 +119,15 @@ __device__ __forceinline__ void acs3_group(uint32_t (&J)[kRegs], float4 (&ring)[
     J[r5] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e[5] : e[5], e[5], m));
     J[r6] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e[6] : e[6], e[6], m));
     J[r7] = __float_as_uint(__builtin_fmaf(WEIGHTED ? dt * e[7] : e[7], e[7], m));
+    // order within the group: the minimums and compares, then the scalar assembly of the
+    // three index bits interleaved one for one with the independent vector work (with two
+    // waves per SIMD the compare -> SALU -> carry-in chain is otherwise exposed)
+    __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x004, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+    }
 }
 
 template <int SEG, bool WEIGHTED, int NM, int... I>
