@@ -6,8 +6,9 @@ log2(n) butterfly levels plus the 1/sqrt(n) and sign multiplies, all in fp32, so
 output's chunk).
 
 Scale field (tcq_scale_field): a_r sums N squares per row (a lane sums N/256 of them,
-then 8 tree additions), b_c sums M squares of W/a per column (slabs of M/64 rows, then 64
-slab sums), each followed by a division and a square root; relative bounds
+then 8 tree additions; with 16-byte loads a lane keeps four sums of N/1024 terms and adds
+them pairwise, a shorter chain), b_c sums M squares of W/a per column (slabs of M/64 rows,
+then 64 slab sums), each followed by a division and a square root; relative bounds
   a: (N/256 + 16) u,   b: (M/64 + 64 + N/256 + 32) u,   Wn: (bound_a + bound_b + 4) u.
 """
 import sys

@@ -207,6 +207,32 @@ __global__ __launch_bounds__(256) void row_rms_kernel(const float *__restrict__ 
     }
 }
 
+// The same with 16-byte loads (N % 4 == 0, 16-byte aligned rows): a lane keeps four
+// partial sums, one per component (N/1024 terms each), added pairwise before the tree.
+__global__ __launch_bounds__(256) void row_rms4_kernel(const float *__restrict__ W,
+                                                       int64_t ldw, int64_t N,
+                                                       float *__restrict__ a) {
+    __shared__ float part[4];
+    const int64_t r = blockIdx.x;
+    const float4 *w = reinterpret_cast<const float4 *>(W + r * ldw);
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    for (int64_t q = threadIdx.x; q < N / 4; q += 256) {
+        const float4 v = w[q];
+        s0 = __builtin_fmaf(v.x, v.x, s0);
+        s1 = __builtin_fmaf(v.y, v.y, s1);
+        s2 = __builtin_fmaf(v.z, v.z, s2);
+        s3 = __builtin_fmaf(v.w, v.w, s3);
+    }
+    float s = (s0 + s1) + (s2 + s3);
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+        a[r] = tot > 0.0f ? __builtin_sqrtf(tot / static_cast<float>(N)) : 1.0f;
+    }
+}
+
 // Column sums of (W_rc / a_r)^2 over row slab blockIdx.y, rows in ascending order.
 __global__ __launch_bounds__(256) void col_partial_kernel(
     const float *__restrict__ W, int64_t ldw, int64_t M, int64_t N, int64_t slab_rows,
@@ -261,6 +287,25 @@ __global__ __launch_bounds__(256) void scale_apply_kernel(
     for (int64_t c = static_cast<int64_t>(blockIdx.y) * 256 + threadIdx.x; c < N;
          c += static_cast<int64_t>(gridDim.y) * 256)
         Wn[r * ldn + c] = W[r * ldw + c] / (ar * b[c]);
+}
+
+// The same with 16-byte accesses (N % 4 == 0, 16-byte aligned rows and b); the
+// arithmetic per element is unchanged.
+__global__ __launch_bounds__(256) void scale_apply4_kernel(
+    const float *__restrict__ W, int64_t ldw, int64_t N, const float *__restrict__ a,
+    const float *__restrict__ b, float *__restrict__ Wn, int64_t ldn) {
+    const int64_t r = blockIdx.x;
+    const float ar = a[r];
+    const float4 *w = reinterpret_cast<const float4 *>(W + r * ldw);
+    const float4 *b4 = reinterpret_cast<const float4 *>(b);
+    float4 *o = reinterpret_cast<float4 *>(Wn + r * ldn);
+    for (int64_t q = static_cast<int64_t>(blockIdx.y) * 256 + threadIdx.x; q < N / 4;
+         q += static_cast<int64_t>(gridDim.y) * 256) {
+        const float4 v = w[q];
+        const float4 bc = b4[q];
+        o[q] = make_float4(v.x / (ar * bc.x), v.y / (ar * bc.y), v.z / (ar * bc.z),
+                           v.w / (ar * bc.w));
+    }
 }
 
 template <int F>
@@ -327,8 +372,17 @@ hipError_t launch_hadamard(const float *X, int64_t ldx, float *Y, int64_t ldy, i
 
 hipError_t launch_scale_field(const float *W, int64_t ldw, int64_t M, int64_t N, float *a,
                               float *b, float *Wn, int64_t ldn, float *part, hipStream_t s) {
-    hipLaunchKernelGGL(row_rms_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, s, W, ldw,
-                       N, a);
+    // 16-byte accesses where every row (and b) is 16-byte aligned
+    const bool v4 = N % 4 == 0 && ldw % 4 == 0 &&
+                    (reinterpret_cast<uintptr_t>(W) & 15u) == 0 &&
+                    (reinterpret_cast<uintptr_t>(b) & 15u) == 0 &&
+                    (!Wn || (ldn % 4 == 0 && (reinterpret_cast<uintptr_t>(Wn) & 15u) == 0));
+    if (v4)
+        hipLaunchKernelGGL(row_rms4_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, s, W,
+                           ldw, N, a);
+    else
+        hipLaunchKernelGGL(row_rms_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, s, W,
+                           ldw, N, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t nslabs = static_cast<int64_t>(scale_field_slabs(M));
@@ -343,6 +397,14 @@ hipError_t launch_scale_field(const float *W, int64_t ldw, int64_t M, int64_t N,
                        part, static_cast<int>(nslabs), M, N, b);
     e = hipGetLastError();
     if (e != hipSuccess || !Wn) return e;
+    if (v4) {
+        const int64_t cb4 = (N / 4 + 255) / 256;
+        const int64_t gy4 = cb4 < 16 ? cb4 : 16;
+        hipLaunchKernelGGL(scale_apply4_kernel, dim3(static_cast<unsigned>(M),
+                           static_cast<unsigned>(gy4)), dim3(256), 0, s, W, ldw, N, a, b, Wn,
+                           ldn);
+        return hipGetLastError();
+    }
     const int64_t gy = cb < 16 ? cb : 16;
     hipLaunchKernelGGL(scale_apply_kernel, dim3(static_cast<unsigned>(M),
                        static_cast<unsigned>(gy)), dim3(256), 0, s, W, ldw, N, a, b, Wn, ldn);
