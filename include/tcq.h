@@ -240,7 +240,8 @@ int tcq_bcjr(const float *W, int64_t M, int64_t N, int64_t ldw, const float *d,
  *   n          : power of two, n <= 4096; n divides len; if n < 64 then len <= 8192
  *   sigma      : device, len floats (+1/-1), or NULL for all +1
  *   Y, ldy     : device output; Y == X (with ldy == ldx) works in place
- * fp32 butterflies; |error| <= (log2(n) + 2) u sum|x_i| / sqrt(n) per output.
+ * fp32 butterflies; |error| <= (log2(n) + 3) u sum|x_i| / sqrt(n) per output, u = 2^-24
+ * (log2(n) butterfly levels, the rounded 1/sqrt(n), its multiply and the sign multiply).
  * Errors: TCQ_EINVAL, TCQ_EUNSUPPORTED, TCQ_EHIP.
  */
 int tcq_hadamard(const float *X, int64_t rows, int64_t len, int64_t ldx, int64_t n,

@@ -168,3 +168,99 @@ def test_workspace_sizes():
     assert small >= 64 * 64 * 64 * 2 // 8
     with pytest.raises(tcq.TcqError):
         tcq.tcq_encode_workspace_bytes(10, 100, 16, 2, 1, 256)
+
+
+def test_bcjr_argument_checks():
+    lib = _lib.load()
+    E = _lib
+
+    def run(**kw):
+        a = dict(W=FAKE, M=2, N=512, ldw=512, d=None, cb=FAKE, L=16, k=2, V=1, T=256,
+                 tau=0.1, soft=FAKE, ldo=512, logz=None, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.tcq_bcjr(a["W"], a["M"], a["N"], a["ldw"], a["d"], a["cb"], a["L"],
+                            a["k"], a["V"], a["T"], a["tau"], a["soft"], a["ldo"], a["logz"],
+                            a["ws"], a["wsb"], None)
+
+    assert run(N=500) == E.TCQ_EINVAL                     # N % T
+    assert run(k=3, V=2, T=256) == E.TCQ_EUNSUPPORTED     # k*V = 6 > 4
+    assert "k*V" in tcq.tcq_last_error()
+    assert run(tau=0.0) == E.TCQ_EINVAL
+    assert run(tau=-1.0) == E.TCQ_EINVAL
+    assert run(tau=float("inf")) == E.TCQ_EINVAL
+    assert run(tau=float("nan")) == E.TCQ_EINVAL
+    assert run(tau=1e-39) == E.TCQ_EINVAL                  # -log2(e)/tau overflows fp32
+    assert run(W=None) == E.TCQ_EINVAL
+    assert run(cb=None) == E.TCQ_EINVAL
+    assert run(soft=None) == E.TCQ_EINVAL
+    assert run(ldw=100) == E.TCQ_EINVAL
+    assert run(ldo=100) == E.TCQ_EINVAL
+    assert run(wsb=16) == E.TCQ_EWORKSPACE
+    assert run(ws=None) == E.TCQ_EWORKSPACE
+    assert run(M=0) == E.TCQ_OK
+    assert tcq.tcq_last_error() == ""
+    size = ctypes_size()
+    assert lib.tcq_bcjr_workspace_bytes(2, 512, 16, 2, 1, 256, size) == E.TCQ_OK
+    # at least one block: T/V steps of 2^(L-kV) floats (the stored forward vectors)
+    assert size.contents.value >= 256 * (1 << 14) * 4
+    assert lib.tcq_bcjr_workspace_bytes(2, 512, 16, 4, 2, 256, size) == E.TCQ_EUNSUPPORTED
+
+
+def test_hadamard_argument_checks():
+    lib = _lib.load()
+    E = _lib
+
+    def run(**kw):
+        a = dict(X=FAKE, rows=2, len=2048, ldx=2048, n=2048, sigma=None, inverse=0,
+                 Y=FAKE + (1 << 24), ldy=2048)
+        a.update(kw)
+        return lib.tcq_hadamard(a["X"], a["rows"], a["len"], a["ldx"], a["n"], a["sigma"],
+                                a["inverse"], a["Y"], a["ldy"], None)
+
+    assert run(n=3) == E.TCQ_EINVAL                       # not a power of two
+    assert run(n=0) == E.TCQ_EINVAL
+    assert run(rows=-1) == E.TCQ_EINVAL
+    assert run(len=3000, ldx=3000, ldy=3000) == E.TCQ_EINVAL   # n does not divide len
+    assert run(n=8192, len=8192, ldx=8192, ldy=8192) == E.TCQ_EUNSUPPORTED
+    assert run(n=32, len=16384, ldx=16384, ldy=16384) == E.TCQ_EUNSUPPORTED
+    assert run(X=None) == E.TCQ_EINVAL
+    assert run(Y=None) == E.TCQ_EINVAL
+    assert run(ldx=1000) == E.TCQ_EINVAL
+    assert run(Y=FAKE + 4) == E.TCQ_EINVAL                # overlapping, not the same buffer
+    assert "overlap" in tcq.tcq_last_error()
+    assert run(Y=FAKE, ldy=4096, ldx=2048) == E.TCQ_EINVAL  # in place needs ldx == ldy
+    assert run(rows=0) == E.TCQ_OK
+    assert run(len=0, ldx=0, ldy=0) == E.TCQ_OK
+
+
+def test_scale_field_argument_checks():
+    lib = _lib.load()
+    E = _lib
+
+    def run(**kw):
+        a = dict(W=FAKE, M=4, N=256, ldw=256, a=FAKE, b=FAKE, Wn=None, ldn=256, ws=FAKE,
+                 wsb=1 << 40)
+        a.update(kw)
+        return lib.tcq_scale_field(a["W"], a["M"], a["N"], a["ldw"], a["a"], a["b"], a["Wn"],
+                                   a["ldn"], a["ws"], a["wsb"], None)
+
+    assert run(M=-1) == E.TCQ_EINVAL
+    assert run(W=None) == E.TCQ_EINVAL
+    assert run(a=None) == E.TCQ_EINVAL
+    assert run(b=None) == E.TCQ_EINVAL
+    assert run(ldw=100) == E.TCQ_EINVAL
+    assert run(Wn=FAKE, ldn=100) == E.TCQ_EINVAL
+    assert run(wsb=16) == E.TCQ_EWORKSPACE
+    assert run(ws=None) == E.TCQ_EWORKSPACE
+    assert run(M=0) == E.TCQ_OK
+    assert run(N=0) == E.TCQ_OK
+    size = ctypes_size()
+    assert lib.tcq_scale_field_workspace_bytes(4, 256, size) == E.TCQ_OK
+    assert size.contents.value == 4 * 256 * 4                 # one slab per row when M < 64
+    assert lib.tcq_scale_field_workspace_bytes(4096, 256, size) == E.TCQ_OK
+    assert size.contents.value == 64 * 256 * 4                # 64 slabs of column sums
+
+
+def ctypes_size():
+    import ctypes
+    return ctypes.pointer(ctypes.c_size_t(0))
