@@ -51,12 +51,15 @@ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 // whole steps; every block's stream is a whole number of units, so step q of row unit u
 // is step g = u S + q of the row and multiplies x[g V + v].  x is staged once per
 // workgroup in LDS in the order [tile of 64 units][q][lane][v], which makes the reads of
-// a wave for one q contiguous.  One wave per row at a time, lane l owning units l,
-// l + 64, ...; the 64 lane sums meet in a shuffle tree.  A step whose state is in
+// a wave for one q contiguous.  R waves share a row (R = 1 unless the rows are too few
+// to give every CU a workgroup): wave r of the group takes the row's tiles of 64 units
+// r, r + R, ..., lane l owning the l-th unit of each; the 64 lane sums meet in a shuffle
+// tree, and the R wave sums are added in order through LDS.  A step whose state is in
 // another codebook part multiplies an exact 0 (its table read is masked off), which
 // leaves the sum unchanged.
-template <int KV, int V>
+template <int KV, int V, int R>
 __global__ __launch_bounds__(kGemvThreads) void gemv_tiled_kernel(GemvArgs a) {
+    static_assert(R == 1 || R == 2 || R == 4, "waves per row");
     extern __shared__ float lds[];
     constexpr int U = KV / gcd_c(KV, 32);
     constexpr int S = 32 * U / KV;
@@ -76,8 +79,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_tiled_kernel(GemvArgs a) {
         const int64_t u = (tq / S) * 64 + l;
         xt[j] = (u < upr) ? a.x[(u * S + q) * V + v] : 0.0f;
     }
-    const int64_t gwave = static_cast<int64_t>(blockIdx.x) * kGemvWaves + (tid >> 6);
-    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kGemvWaves;
+    const int wv = tid >> 6;
+    const int rsub = wv & (R - 1);            // this wave's share of its row's tiles
+    constexpr int kRowsPerWg = kGemvWaves / R;
     const uint32_t mask = (1u << a.L) - 1u;
     const uint32_t pmask = static_cast<uint32_t>(per_part - 1);
     const int plog = a.part_log2;
@@ -94,11 +98,16 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_tiled_kernel(GemvArgs a) {
             for (int64_t i = tid; i < per_part * V; i += kGemvThreads) tab[i] = srcf[i];
         }
         __syncthreads();
-        for (int64_t row = gwave; row < a.M; row += nwaves) {
+        // the same number of row iterations in every wave of the workgroup (with R > 1
+        // there are barriers at the end of each)
+        for (int64_t base = static_cast<int64_t>(blockIdx.x) * kRowsPerWg; base < a.M;
+             base += static_cast<int64_t>(gridDim.x) * kRowsPerWg) {
+            const int64_t row = base + wv / R;
             float acc = 0.0f;
-            int64_t c = lane / upb;                      // block of this lane's unit
-            int ju = lane - static_cast<int>(c) * upb;   // unit within the block
-            for (int64_t u0 = 0; u0 < upr; u0 += 64) {
+            const int u1 = rsub * 64 + lane;             // this lane's unit in its first tile
+            int64_t c = u1 / upb;                        // block of this lane's unit
+            int ju = u1 - static_cast<int>(c) * upb;     // unit within the block
+            for (int64_t u0 = rsub * 64; row < a.M && u0 < upr; u0 += 64 * R) {
                 if (u0 + lane < upr) {
                     const int64_t blk = row * a.bpr + c;
                     const uint32_t *wb = a.bits + blk * a.nwords + ju * U;
@@ -131,15 +140,31 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_tiled_kernel(GemvArgs a) {
                             acc = __builtin_fmaf(cv[q][v], xq[q * 64 * V + v], acc);
                     }
                 }
-                c += step_c;
-                ju += step_j;
-                if (ju >= upb) {
-                    ju -= upb;
-                    ++c;
+#pragma unroll
+                for (int t = 0; t < R; ++t) {  // R tiles on
+                    c += step_c;
+                    ju += step_j;
+                    if (ju >= upb) {
+                        ju -= upb;
+                        ++c;
+                    }
                 }
             }
             for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-            if (lane == 0) a.y[row] = (p == 0) ? acc : a.y[row] + acc;
+            if constexpr (R == 1) {
+                if (row < a.M && lane == 0) a.y[row] = (p == 0) ? acc : a.y[row] + acc;
+            } else {
+                // the R wave sums of the row, added in order
+                __shared__ float rpart[kGemvWaves];
+                if (lane == 0) rpart[wv] = acc;
+                __syncthreads();
+                if (rsub == 0 && row < a.M && lane == 0) {
+                    float t = rpart[wv];
+                    for (int q = 1; q < R; ++q) t += rpart[wv + q];
+                    a.y[row] = (p == 0) ? t : a.y[row] + t;
+                }
+                __syncthreads();  // rpart is written again next iteration
+            }
         }
     }
 }
@@ -202,7 +227,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_generic_kernel(GemvArgs a) 
 // Raise a kernel's dynamic LDS limit to the most this file uses, once per kernel (the
 // attribute is process-wide, so later launches skip the runtime call).
 hipError_t allow_lds(const void *kern) {
-    static const void *done[16] = {};
+    static const void *done[48] = {};  // every kernel of this file
     for (const void *k : done)
         if (k == kern) return hipSuccess;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -271,14 +296,20 @@ hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_s
         ++plog;
     a.part_log2 = plog;
     a.parts = 1 << (L - plog);
-    int64_t grid = cu_count();
-    const int64_t need = (M + kGemvWaves - 1) / kGemvWaves;
-    if (grid > need) grid = need;
-    if (grid < 1) grid = 1;
+    const int64_t cus = cu_count();
+    // tiled kernel with rows too few to give every CU a workgroup of one-row waves: R
+    // waves share a row (at most 4, and no more than a row has tiles of 64 units)
+    int rsplit = 1;
+    while (rsplit < 4 && (M * rsplit * 2 + kGemvWaves - 1) / kGemvWaves <= cus &&
+           rsplit * 2 <= tiles)
+        rsplit *= 2;
     const void *kern = reinterpret_cast<const void *>(gemv_generic_kernel);
     if (tiled && (V == 1 || V == 2 || V == 4)) {
-#define TCQ_GEMV_CASE(KV_, V_)                                                     \
-    if (a.kv == KV_ && V == V_) kern = reinterpret_cast<const void *>(gemv_tiled_kernel<KV_, V_>);
+#define TCQ_GEMV_CASE(KV_, V_)                                                            \
+    if (a.kv == KV_ && V == V_)                                                          \
+        kern = rsplit == 4   ? reinterpret_cast<const void *>(gemv_tiled_kernel<KV_, V_, 4>) \
+               : rsplit == 2 ? reinterpret_cast<const void *>(gemv_tiled_kernel<KV_, V_, 2>) \
+                             : reinterpret_cast<const void *>(gemv_tiled_kernel<KV_, V_, 1>);
         TCQ_GEMV_CASE(1, 1)
         TCQ_GEMV_CASE(2, 1)
         TCQ_GEMV_CASE(2, 2)
@@ -300,6 +331,11 @@ hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_s
         a.parts = 1 << (L - plog);
     }
     const bool use_xt = kern != reinterpret_cast<const void *>(gemv_generic_kernel);
+    if (!use_xt) rsplit = 1;  // the generic kernel has one wave per row
+    int64_t grid = cus;
+    const int64_t need = (M * rsplit + kGemvWaves - 1) / kGemvWaves;
+    if (grid > need) grid = need;
+    if (grid < 1) grid = 1;
     const size_t shmem = (size_t{1} << plog) * V * sizeof(float) +
                          (use_xt ? static_cast<size_t>(xt_bytes) : 0);
     hipError_t e = allow_lds(kern);
