@@ -15,6 +15,8 @@
 // deterministic.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "tcq.h"
 #include "tcq_internal.h"
 
@@ -225,9 +227,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_generic_kernel(GemvArgs a) 
 }
 
 // Raise a kernel's dynamic LDS limit to the most this file uses, once per kernel (the
-// attribute is process-wide, so later launches skip the runtime call).
+// attribute is process-wide, so later launches skip the runtime call).  Calls may come
+// from several host threads at once.
 hipError_t allow_lds(const void *kern) {
+    static std::mutex mu;
     static const void *done[48] = {};  // every kernel of this file
+    std::lock_guard<std::mutex> lock(mu);
     for (const void *k : done)
         if (k == kern) return hipSuccess;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -241,19 +246,15 @@ hipError_t allow_lds(const void *kern) {
     return hipSuccess;
 }
 
-int g_cu_count = 0;
-
+// Compute units of the current device (asked on every call: devices of one process, such
+// as partitions of one GPU, need not have the same count).
 int cu_count() {
-    if (g_cu_count == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            n > 0)
-            g_cu_count = n;
-        else
-            g_cu_count = 256;
-    }
-    return g_cu_count;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n > 0)
+        return n;
+    return 256;
 }
 
 }  // namespace
