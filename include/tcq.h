@@ -26,6 +26,8 @@
  *
  * Memory: every pointer argument of tcq_encode / tcq_decode is a DEVICE pointer owned
  * by the caller (for instance torch tensors); the library never frees or retains them.
+ * A workspace argument must start on a 256-byte boundary (every hipMalloc or torch
+ * allocation does); others are rejected with TCQ_EINVAL.
  * Calls are asynchronous on `stream` (0 = the null stream); outputs are valid once the
  * stream has completed.  Argument checks happen on the host, synchronously, before
  * anything is enqueued; a call that returns an error has enqueued nothing.

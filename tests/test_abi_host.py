@@ -82,6 +82,8 @@ def test_encode_argument_checks():
     assert _enc(recon=FAKE, ldr=3) == E.TCQ_EINVAL
     assert _enc(workspace_bytes=16) == E.TCQ_EWORKSPACE
     assert _enc(workspace=None, workspace_bytes=1 << 40) == E.TCQ_EWORKSPACE
+    assert _enc(workspace=FAKE + 4, workspace_bytes=1 << 40) == E.TCQ_EINVAL  # alignment
+    assert "256-byte" in tcq.tcq_last_error()
     assert "workspace" in tcq.tcq_last_error()
     # empty problems are a no-op and touch nothing
     assert _enc(M=0) == E.TCQ_OK
@@ -151,6 +153,7 @@ def test_encode_ldlq_argument_checks():
     assert run(tgt=FAKE, ldt=10) == E.TCQ_EINVAL
     assert run(L=20) == E.TCQ_EUNSUPPORTED
     assert run(wsb=100) == E.TCQ_EWORKSPACE
+    assert run(ws=FAKE + 4) == E.TCQ_EINVAL                   # not 256-byte aligned
     assert run(M=0) == E.TCQ_OK
     assert tcq.tcq_ldlq_workspace_bytes(0, 512, 16, 2, 1, 256) == 0
     big = tcq.tcq_ldlq_workspace_bytes(4, 512, 16, 2, 1, 256)
@@ -197,6 +200,7 @@ def test_bcjr_argument_checks():
     assert run(ldo=100) == E.TCQ_EINVAL
     assert run(wsb=16) == E.TCQ_EWORKSPACE
     assert run(ws=None) == E.TCQ_EWORKSPACE
+    assert run(ws=FAKE + 16) == E.TCQ_EINVAL                 # not 256-byte aligned
     assert run(M=0) == E.TCQ_OK
     assert tcq.tcq_last_error() == ""
     size = ctypes_size()
@@ -252,6 +256,7 @@ def test_scale_field_argument_checks():
     assert run(Wn=FAKE, ldn=100) == E.TCQ_EINVAL
     assert run(wsb=16) == E.TCQ_EWORKSPACE
     assert run(ws=None) == E.TCQ_EWORKSPACE
+    assert run(ws=FAKE + 8) == E.TCQ_EINVAL                  # not 256-byte aligned
     assert run(M=0) == E.TCQ_OK
     assert run(N=0) == E.TCQ_OK
     size = ctypes_size()

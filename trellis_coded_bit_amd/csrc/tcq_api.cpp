@@ -29,6 +29,16 @@ void set_error(const char *fmt, ...) {
 
 static void clear_error() { g_error.clear(); }
 
+// Workspaces must start on a 256-byte boundary (as every hipMalloc or torch allocation
+// does): the kernels lay out their buffers at 256-byte offsets from it.
+static int check_workspace_alignment(const char *fn, const void *workspace) {
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) {
+        set_error("%s: workspace %p is not 256-byte aligned", fn, workspace);
+        return TCQ_EINVAL;
+    }
+    return TCQ_OK;
+}
+
 Plan plan_for(const Problem &p) {
     Plan pl{};
     if (l16_supported(p)) {
@@ -188,6 +198,8 @@ static int encode_impl(const char *fn, const float *W, int64_t M, int64_t N, int
                   workspace ? workspace_bytes : size_t{0}, need);
         return TCQ_EWORKSPACE;
     }
+    rc = check_workspace_alignment(fn, workspace);
+    if (rc != TCQ_OK) return rc;
     int64_t batch = static_cast<int64_t>((workspace_bytes - pl.fixed - 256) / pl.per_block);
     if (batch > p.nblocks) batch = p.nblocks;
     if (batch > (int64_t{1} << 30)) batch = int64_t{1} << 30;
@@ -414,6 +426,8 @@ extern "C" int tcq_encode_ldlq(const float *W, int64_t M, int64_t N, int64_t ldw
                   workspace ? workspace_bytes : size_t{0}, lay.fixed + enc_min);
         return TCQ_EWORKSPACE;
     }
+    rc = check_workspace_alignment(fn, workspace);
+    if (rc != TCQ_OK) return rc;
     char *ws = static_cast<char *>(workspace);
     float *tgt = target ? target : reinterpret_cast<float *>(ws + lay.tgt);
     const int64_t lt = target ? ldt : N;
@@ -510,6 +524,8 @@ extern "C" int tcq_bcjr(const float *W, int64_t M, int64_t N, int64_t ldw, const
                   workspace ? workspace_bytes : size_t{0}, per);
         return TCQ_EWORKSPACE;
     }
+    rc = check_workspace_alignment(fn, workspace);
+    if (rc != TCQ_OK) return rc;
     const int64_t bpr = N / T;
     const int64_t nblocks = M * bpr;
     int64_t batch = static_cast<int64_t>(workspace_bytes / per);
@@ -596,6 +612,8 @@ extern "C" int tcq_scale_field(const float *W, int64_t M, int64_t N, int64_t ldw
                   workspace ? workspace_bytes : size_t{0}, need);
         return TCQ_EWORKSPACE;
     }
+    const int rc = check_workspace_alignment(fn, workspace);
+    if (rc != TCQ_OK) return rc;
     hipError_t e = launch_scale_field(W, ldw, M, N, row_scale, col_scale, Wn, ldn,
                                       static_cast<float *>(workspace), stream);
     if (e != hipSuccess) return hip_fail(fn, "scale-field launch", e);
