@@ -45,35 +45,43 @@ __global__ __launch_bounds__(256) void ldlq_update_kernel(
             acc[a][b] = (r < M && c < c_end) ? tgt[r * ldt + c] : 0.0f;
         }
     }
-    for (int ib = 0; ib < T; ib += kChunk) {
+    // The next chunk's W, what and U values are requested into registers before the
+    // current chunk is computed, so the global-memory latency overlaps the fmaf work.
+    float pw[4], ph[4], pu[4];
+    auto fetch = [&](int ib) {
         const int nk = (T - ib < kChunk) ? T - ib : kChunk;
-        __syncthreads();
-        // E tile: 64 rows x 16 terms, read along a row (contiguous in i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+            // E tile: 64 rows x 16 terms, read along a row (contiguous in i)
             const int idx = tid + 256 * q;
             const int rr = idx >> 4;
             const int ii = idx & 15;
             const int64_t r = r0 + rr;
-            float e = 0.0f;
+            pw[q] = 0.0f;
+            ph[q] = 0.0f;
             if (r < M && ii < nk) {
-                const int64_t i = i0 + ib + ii;
-                e = W[r * ldw + i] - what[r * ldh + (ib + ii)];
+                pw[q] = W[r * ldw + i0 + ib + ii];
+                ph[q] = what[r * ldh + (ib + ii)];
             }
-            Es[ii][rr] = e;
+            // U tile: 16 terms x 64 columns, read along a row of U (contiguous in c)
+            const int ui = idx >> 6;
+            const int cc = idx & 63;
+            const int64_t c = c0 + cc;
+            pu[q] = (ui < nk && c < c_end) ? U[(i0 + ib + ui) * ldu + c] : 0.0f;
         }
-        // U tile: 16 terms x 64 columns, read along a row of U (contiguous in c)
+    };
+    fetch(0);
+    for (int ib = 0; ib < T; ib += kChunk) {
+        const int nk = (T - ib < kChunk) ? T - ib : kChunk;
+        __syncthreads();  // every thread is done with the previous chunk
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int idx = tid + 256 * q;
-            const int ii = idx >> 6;
-            const int cc = idx & 63;
-            const int64_t c = c0 + cc;
-            float u = 0.0f;
-            if (ii < nk && c < c_end) u = U[(i0 + ib + ii) * ldu + c];
-            Us[ii][cc] = u;
+            Es[idx & 15][idx >> 4] = pw[q] - ph[q];  // zero outside the tile (0 - 0)
+            Us[idx >> 6][idx & 63] = pu[q];
         }
         __syncthreads();
+        if (ib + kChunk < T) fetch(ib + kChunk);
         for (int ii = 0; ii < nk; ++ii) {
             float e[4], u[4];
 #pragma unroll
