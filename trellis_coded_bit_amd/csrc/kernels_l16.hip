@@ -27,6 +27,12 @@ namespace {
 
 using namespace l16;
 
+// Context with the backpointer words addressed through a buffer descriptor (lane offset in
+// a register, step and half in the scalar offset): no 64-bit address per store.
+struct CtxL : Ctx {
+    BpBuf bpb;
+};
+
 constexpr int kPrefetch = 12;                           // groups of codebook in flight
 
 __global__ __launch_bounds__(256) void l16_prepare_kernel(const float *__restrict__ C,
@@ -118,11 +124,11 @@ __device__ __forceinline__ void acs_group(uint32_t (&J)[kRegs], float4 (&ring)[k
 template <int SEG, bool WEIGHTED, int NM, int... I>
 __device__ __forceinline__ void acs_segment_impl(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
                                                  __amdgpu_buffer_rsrc_t rs, uint32_t voff,
-                                                 float wt, float dt, uint32_t *bp_word,
-                                                 std::integer_sequence<int, I...>) {
+                                                 float wt, float dt, const BpBuf &bpb,
+                                                 int bp_word, std::integer_sequence<int, I...>) {
     uint32_t acc = 0;
     (acs_group<SEG, WEIGHTED, NM, I>(J, ring, rs, voff, wt, dt, acc), ...);
-    *bp_word = acc;
+    bpb.store(bp_word, acc);
 }
 
 // Groups I0 .. I0 + 7 of segment SEG, their backpointer bits shifted into acc (the word
@@ -137,7 +143,7 @@ __device__ __forceinline__ void acs_half_impl(uint32_t (&J)[kRegs], float4 (&rin
 
 template <int SEG, bool WEIGHTED, int NM, int I0>
 __device__ __forceinline__ void acs_half(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
-                                         const Ctx &cx, const StepIn &in, uint32_t &acc) {
+                                         const CtxL &cx, const StepIn &in, uint32_t &acc) {
     constexpr int P = seg_step(SEG);
     acs_half_impl<SEG, WEIGHTED, NM, I0>(J, ring, cx.rs, cx.voff, in.w[P - 1], in.d[P - 1],
                                          acc, std::make_integer_sequence<int, 8>{});
@@ -145,11 +151,11 @@ __device__ __forceinline__ void acs_half(uint32_t (&J)[kRegs], float4 (&ring)[kP
 
 template <int SEG, bool WEIGHTED, int NM>
 __device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
-                                            const Ctx &cx, int t0, const StepIn &in) {
+                                            const CtxL &cx, int t0, const StepIn &in) {
     constexpr int P = seg_step(SEG);
     const int t = t0 + P - 1;  // 0-based step index
     acs_segment_impl<SEG, WEIGHTED, NM>(J, ring, cx.rs, cx.voff, in.w[P - 1], in.d[P - 1],
-                                        cx.bp + 2 * kThreads * t + seg_half(SEG),
+                                        cx.bpb, 2 * kThreads * t + seg_half(SEG),
                                         std::make_integer_sequence<int, 16>{});
 }
 
@@ -160,18 +166,18 @@ __device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)
 constexpr int kReadAhead = 3;
 template <bool WEIGHTED, int NM, int I>
 __device__ __forceinline__ void seg2_group(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
-                                           const Ctx &cx, float wt, float dt, uint32_t &acc) {
+                                           const CtxL &cx, float wt, float dt, uint32_t &acc) {
     if constexpr (I + kReadAhead < 16) round_read_group<1 - NM, 1, I + kReadAhead>(J, cx);
     acs_group<2, WEIGHTED, NM, I>(J, ring, cx.rs, cx.voff, wt, dt, acc);
 }
 template <bool WEIGHTED, int NM, int... I>
 __device__ __forceinline__ void seg2_reading(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
-                                             const Ctx &cx, int t0, const StepIn &in,
+                                             const CtxL &cx, int t0, const StepIn &in,
                                              std::integer_sequence<int, I...>) {
     round_read_groups<1 - NM, 1>(J, cx, std::make_integer_sequence<int, kReadAhead>{});
     uint32_t acc = 0;
     (seg2_group<WEIGHTED, NM, I>(J, ring, cx, in.w[0], in.d[0], acc), ...);
-    cx.bp[2 * kThreads * t0 + seg_half(2)] = acc;
+    cx.bpb.store(2 * kThreads * t0 + seg_half(2), acc);
 }
 
 // Super-step (steps t0+1 .. t0+3) under naming NM, with the weights (and d) of its three
@@ -181,7 +187,7 @@ __device__ __forceinline__ void seg2_reading(uint32_t (&J)[kRegs], float4 (&ring
 // round 1 left in LDS.
 template <bool WEIGHTED, int NM>
 __device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
-                                           const Ctx &cx, int t0, const StepIn &in,
+                                           const CtxL &cx, int t0, const StepIn &in,
                                            StepIn &next) {
     acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
     acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0, in);
@@ -199,7 +205,7 @@ __device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[
     __syncthreads();  // round-0 values written by every wave
     round_read<NM, 0>(J, cx);
     acs_half<5, WEIGHTED, NM, 8>(J, ring, cx, in, acc5);
-    cx.bp[2 * kThreads * (t0 + 2) + seg_half(5)] = acc5;
+    cx.bpb.store(2 * kThreads * (t0 + 2) + seg_half(5), acc5);
     __syncthreads();  // every wave has read round 0
     round_write<NM, 1>(J, cx);
 }
@@ -208,7 +214,7 @@ __device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[
 // where the order departs from a full super-step).
 template <bool WEIGHTED, int NM, int R>
 __device__ __forceinline__ void tail_steps(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
-                                           const Ctx &cx, int t0, const StepIn &in) {
+                                           const CtxL &cx, int t0, const StepIn &in) {
     acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
     if constexpr (R == 2) acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0, in);
     __syncthreads();
@@ -247,8 +253,10 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     const int64_t row = blk / blocks_per_row;
     const int64_t col = blk % blocks_per_row;
 
-    const Ctx cx = make_ctx(W, ldw, WEIGHTED ? d : nullptr, cb, n, row, col, w, l,
-                            bp + blockIdx.x * bp_per_block);
+    CtxL cx;
+    static_cast<Ctx &>(cx) = make_ctx(W, ldw, WEIGHTED ? d : nullptr, cb, n, row, col, w, l,
+                                      bp + blockIdx.x * bp_per_block);
+    cx.bpb = make_bpbuf(bp + blockIdx.x * bp_per_block, bp_per_block, w, l);
 
     uint32_t J[kRegs];  // fp32 costs held as their bit patterns
 #pragma unroll
