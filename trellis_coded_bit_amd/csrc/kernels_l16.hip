@@ -33,7 +33,11 @@ struct CtxL : Ctx {
     BpBuf bpb;
 };
 
-constexpr int kPrefetch = 12;                           // groups of codebook in flight
+// Groups of codebook in flight.  Measured on MI355X: at d = 1 a 12-deep ring beats a
+// 16-deep one (41.7 against 42.0 ms at 2048 x 2048); the weighted search, with one more
+// multiply per update between the loads, gains 0.6 % from the deeper ring.
+template <bool WEIGHTED>
+constexpr int kRing = WEIGHTED ? 16 : 12;
 
 __global__ __launch_bounds__(256) void l16_prepare_kernel(const float *__restrict__ C,
                                                           float4 *__restrict__ out) {
@@ -63,12 +67,13 @@ __device__ __forceinline__ float4 cb_load(__amdgpu_buffer_rsrc_t rs, uint32_t vo
 }
 
 // The codebook entries are consumed in the fixed segment order of a super-step
-// (position k = 16 * segment + i, 96 per super-step); a ring of kPrefetch loads runs
+// (position k = 16 * segment + i, 96 per super-step); a ring of D loads runs
 // ahead of the consumer, across segment and super-step boundaries.
 constexpr int kPositions = 96;
-// the ring runs across super-steps: position k lives in slot k mod kPrefetch in every
+// the ring runs across super-steps: position k lives in slot k mod D in every
 // super-step only if the ring size divides the positions per super-step
-static_assert(kPositions % kPrefetch == 0, "ring size must divide a super-step");
+static_assert(kPositions % kRing<false> == 0 && kPositions % kRing<true> == 0,
+              "ring size must divide a super-step");
 
 template <int K>
 __device__ __forceinline__ float4 cb_load_pos(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
@@ -76,17 +81,17 @@ __device__ __forceinline__ float4 cb_load_pos(__amdgpu_buffer_rsrc_t rs, uint32_
     return cb_load<seg_step(k / 16)>(rs, voff, seg_group(k / 16, k % 16));
 }
 
-template <int K0, int... I>
-__device__ __forceinline__ void ring_prime(float4 (&ring)[kPrefetch], __amdgpu_buffer_rsrc_t rs,
+template <int K0, int D, int... I>
+__device__ __forceinline__ void ring_prime(float4 (&ring)[D], __amdgpu_buffer_rsrc_t rs,
                                            uint32_t voff, std::integer_sequence<int, I...>) {
-    ((ring[(K0 + I) % kPrefetch] = cb_load_pos<K0 + I>(rs, voff)), ...);
+    ((ring[(K0 + I) % D] = cb_load_pos<K0 + I>(rs, voff)), ...);
 }
 
-// Fill the ring with positions K0 .. K0 + kPrefetch - 1.
-template <int K0>
-__device__ __forceinline__ void ring_fill(float4 (&ring)[kPrefetch], __amdgpu_buffer_rsrc_t rs,
+// Fill the ring with positions K0 .. K0 + D - 1.
+template <int K0, int D>
+__device__ __forceinline__ void ring_fill(float4 (&ring)[D], __amdgpu_buffer_rsrc_t rs,
                                           uint32_t voff) {
-    ring_prime<K0>(ring, rs, voff, std::make_integer_sequence<int, kPrefetch>{});
+    ring_prime<K0>(ring, rs, voff, std::make_integer_sequence<int, D>{});
 }
 
 // Path costs are non-negative floats (sums of d * e * e >= 0 starting from +0, never
@@ -96,17 +101,18 @@ __device__ __forceinline__ void ring_fill(float4 (&ring)[kPrefetch], __amdgpu_bu
 // One group (I-th of segment SEG) under register naming NM.  `wt`/`dt` are the step's
 // weight and d; two backpointer bits are shifted into `acc`.
 template <int SEG, bool WEIGHTED, int NM, int I>
-__device__ __forceinline__ void acs_group(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+__device__ __forceinline__ void acs_group(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                           __amdgpu_buffer_rsrc_t rs, uint32_t voff, float wt,
                                           float dt, uint32_t &acc) {
     constexpr int P = seg_step(SEG);
     constexpr int k = 16 * SEG + I;
     constexpr uint32_t g = seg_group(SEG, I);
-    // at most kPrefetch codebook loads in flight: later loads stay below this point
+    // at most kRing codebook loads in flight: later loads stay below this point
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    const float4 c = ring[k % kPrefetch];
-    ring[k % kPrefetch] = cb_load_pos<k + kPrefetch>(rs, voff);
+    constexpr int D = kRing<WEIGHTED>;
+    const float4 c = ring[k % D];
+    ring[k % D] = cb_load_pos<k + D>(rs, voff);
     constexpr int r0 = phys(NM, group_reg(P, g, 0)), r1 = phys(NM, group_reg(P, g, 1));
     constexpr int r2 = phys(NM, group_reg(P, g, 2)), r3 = phys(NM, group_reg(P, g, 3));
     const uint32_t u0 = J[r0], u1 = J[r1], u2 = J[r2], u3 = J[r3];
@@ -122,7 +128,8 @@ __device__ __forceinline__ void acs_group(uint32_t (&J)[kRegs], float4 (&ring)[k
 }
 
 template <int SEG, bool WEIGHTED, int NM, int... I>
-__device__ __forceinline__ void acs_segment_impl(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+__device__ __forceinline__ void acs_segment_impl(uint32_t (&J)[kRegs],
+                                                 float4 (&ring)[kRing<WEIGHTED>],
                                                  __amdgpu_buffer_rsrc_t rs, uint32_t voff,
                                                  float wt, float dt, const BpBuf &bpb,
                                                  int bp_word, std::integer_sequence<int, I...>) {
@@ -134,7 +141,7 @@ __device__ __forceinline__ void acs_segment_impl(uint32_t (&J)[kRegs], float4 (&
 // Groups I0 .. I0 + 7 of segment SEG, their backpointer bits shifted into acc (the word
 // is stored by the caller once all 16 groups are in).
 template <int SEG, bool WEIGHTED, int NM, int I0, int... I>
-__device__ __forceinline__ void acs_half_impl(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+__device__ __forceinline__ void acs_half_impl(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                               __amdgpu_buffer_rsrc_t rs, uint32_t voff, float wt,
                                               float dt, uint32_t &acc,
                                               std::integer_sequence<int, I...>) {
@@ -142,7 +149,7 @@ __device__ __forceinline__ void acs_half_impl(uint32_t (&J)[kRegs], float4 (&rin
 }
 
 template <int SEG, bool WEIGHTED, int NM, int I0>
-__device__ __forceinline__ void acs_half(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+__device__ __forceinline__ void acs_half(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                          const CtxL &cx, const StepIn &in, uint32_t &acc) {
     constexpr int P = seg_step(SEG);
     acs_half_impl<SEG, WEIGHTED, NM, I0>(J, ring, cx.rs, cx.voff, in.w[P - 1], in.d[P - 1],
@@ -150,7 +157,7 @@ __device__ __forceinline__ void acs_half(uint32_t (&J)[kRegs], float4 (&ring)[kP
 }
 
 template <int SEG, bool WEIGHTED, int NM>
-__device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+__device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                             const CtxL &cx, int t0, const StepIn &in) {
     constexpr int P = seg_step(SEG);
     const int t = t0 + P - 1;  // 0-based step index
@@ -165,13 +172,13 @@ __device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)
 // wait counter counts at most 15) and each group waits only for its own values.
 constexpr int kReadAhead = 3;
 template <bool WEIGHTED, int NM, int I>
-__device__ __forceinline__ void seg2_group(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+__device__ __forceinline__ void seg2_group(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                            const CtxL &cx, float wt, float dt, uint32_t &acc) {
     if constexpr (I + kReadAhead < 16) round_read_group<1 - NM, 1, I + kReadAhead>(J, cx);
     acs_group<2, WEIGHTED, NM, I>(J, ring, cx.rs, cx.voff, wt, dt, acc);
 }
 template <bool WEIGHTED, int NM, int... I>
-__device__ __forceinline__ void seg2_reading(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+__device__ __forceinline__ void seg2_reading(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                              const CtxL &cx, int t0, const StepIn &in,
                                              std::integer_sequence<int, I...>) {
     round_read_groups<1 - NM, 1>(J, cx, std::make_integer_sequence<int, kReadAhead>{});
@@ -186,7 +193,7 @@ __device__ __forceinline__ void seg2_reading(uint32_t (&J)[kRegs], float4 (&ring
 // hold round 0); on exit the costs have been transposed again for naming 1 - NM, with
 // round 1 left in LDS.
 template <bool WEIGHTED, int NM>
-__device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+__device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                            const CtxL &cx, int t0, const StepIn &in,
                                            StepIn &next) {
     acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
@@ -213,7 +220,7 @@ __device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[
 // The last R = 1 or 2 steps (segments 0..3 in order; for one step the ring is refilled
 // where the order departs from a full super-step).
 template <bool WEIGHTED, int NM, int R>
-__device__ __forceinline__ void tail_steps(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch],
+__device__ __forceinline__ void tail_steps(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                            const CtxL &cx, int t0, const StepIn &in) {
     acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
     if constexpr (R == 2) acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0, in);
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     uint32_t J[kRegs];  // fp32 costs held as their bit patterns
 #pragma unroll
     for (int r = 0; r < kRegs; ++r) J[r] = 0u;
-    float4 ring[kPrefetch];
+    float4 ring[kRing<WEIGHTED>];
     ring_fill<0>(ring, cx.rs, cx.voff);
 
     // Every super-step ends with a transposition whose second round is read at the start
