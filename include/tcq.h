@@ -70,8 +70,8 @@ int tcq_version(void);
 const char *tcq_last_error(void);
 
 /*
- * tcq_make_codebook -- the closed-form quantile table (CurveTQ abstract: "closed-form
- * quantile table"), in a seeded shuffled order.
+ * tcq_make_codebook -- the closed-form quantile table that the CurveTQ abstract names, in a
+ * seeded shuffled order.
  *   L, V      : 1 <= L <= 24, 1 <= V <= min(L, 8)
  *   seed      : shuffle seed
  *   out_host  : HOST buffer of 2^L * V floats, row-major [2^L][V]; written entirely.

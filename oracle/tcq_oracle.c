@@ -12,7 +12,7 @@
  *  - The state picks the allowed subset of values, the written bits pick a value inside
  *    it and also set the next state (Pingala-8 post, the trellis-coded quantization
  *    paragraph and its 1-bit toy example).
- *  - The cost is a sum of squared errors (same toy: scalar rounding "scores 1.42").
+ *  - The cost is a sum of squared errors (same toy: plain rounding totals 1.42).
  *  - Each squared error is weighted by d_i, the diagonal of the Hessian's LDL factor,
  *    inside the Viterbi branch metric, and each coding block carries its own start
  *    state (CurveTQ abstract on the aqora listing).

@@ -1,5 +1,5 @@
 // tcq_make_codebook: the closed-form Gaussian quantile table in a seeded order
-// (CurveTQ abstract on the aqora listing names a "closed-form quantile table"; the
+// (the CurveTQ abstract on the aqora listing names a closed-form quantile table; the
 // QTIP abstract names lookup-only trellis codes).  Host code, no GPU involvement.
 #include <cmath>
 #include <cstdint>
