@@ -67,8 +67,9 @@ SMALL = [
 
 # L = 16 register-resident kernels: every combination of super-step count parity and
 # leftover steps (k*V = 2: three steps per super-step; k*V = 3: two; k*V = 4: three
-# 2-bit half-steps, i.e. 2n half-steps for n steps)
-L16_EDGES = [(16, 2, 1, n, 2, 2 * n, n % 2 == 0) for n in range(1, 13)] + \
+# 2-bit half-steps, i.e. 2n half-steps for n steps).  For k*V = 2 both the plain and the
+# weighted kernel (which keep different numbers of codebook loads in flight) run every n.
+L16_EDGES = [(16, 2, 1, n, 2, 2 * n, w) for n in range(1, 13) for w in (False, True)] + \
             [(16, 3, 1, n, 2, 2 * n, n % 2 == 1) for n in range(1, 9)] + \
             [(16, 3, 1, 256, 3, 768, True), (16, 3, 1, 255, 1, 510, False)] + \
             [(16, 2, 2, 2 * n, 2, 4 * n, n % 2 == 1) for n in range(1, 13)] + \
