@@ -77,7 +77,9 @@ L16_EDGES = [(16, 2, 1, n, 2, 2 * n, w) for n in range(1, 13) for w in (False, T
             [(16, 2, 2, 256, 2, 512, True), (16, 2, 2, 254, 1, 508, False),
              (16, 4, 1, 256, 1, 512, True)] + \
             [(16, 2, 1, 1024, 1, 1024, True), (16, 2, 1, 1022, 1, 1022, False),
-             (16, 3, 1, 1024, 1, 1024, True), (16, 2, 2, 1024, 1, 1024, False)]  # longest blocks
+             (16, 3, 1, 1024, 1, 1024, True), (16, 2, 2, 1024, 1, 1024, False)] + \
+            [(16, 2, 2, 2048, 1, 2048, True), (16, 4, 1, 1024, 1, 1024, False)]  # longest blocks
+# (the last two have 1024 steps, i.e. 2048 2-bit half-steps in the traceback)
 
 
 @pytest.mark.parametrize("L,k,V,T,M,N,weighted", SMALL + L16_EDGES)
