@@ -73,6 +73,11 @@ CASES = [
     (16, 2, 1, 256, 70, 256),
     (12, 2, 1, 64, 4500, 512),   # many short rows: two rows per wave
     (16, 4, 1, 256, 9, 2048),
+    # longest blocks (1024 steps)
+    (16, 2, 2, 2048, 2, 4096),
+    (16, 4, 1, 1024, 2, 2048),
+    (16, 2, 1, 1024, 3, 2048),
+    (16, 3, 1, 1024, 2, 2048),
 ]
 
 
