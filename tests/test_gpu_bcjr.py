@@ -93,6 +93,16 @@ def test_bcjr_parity(oracle_lib, L, k, V, T, M, N, weighted, tau):
     _say(f"  worst error / tolerance {worst:.3f}")
 
 
+@pytest.mark.parametrize("L,k,V,T,M,N,weighted", [
+    (16, 3, 1, 1024, 1, 1024, True),    # 1024 steps of 8 predecessors
+    (16, 2, 2, 2048, 1, 2048, False),   # 1024 steps of k*V = 4 (16 predecessors)
+])
+def test_bcjr_parity_longest(oracle_lib, L, k, V, T, M, N, weighted):
+    """The longest blocks for k*V = 3 and 4 at one temperature (the float64 oracle takes
+    about 20 and 40 s per block)."""
+    test_bcjr_parity(oracle_lib, L, k, V, T, M, N, weighted, 0.1)
+
+
 def test_bcjr_low_temperature_is_viterbi(oracle_lib):
     """tau far below the runner-up gap: the soft codeword is the Viterbi reconstruction."""
     import oracle
