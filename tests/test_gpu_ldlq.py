@@ -100,6 +100,8 @@ CASES = [
     (16, 2, 1, 256, 2, 768, False),
     (16, 3, 1, 256, 2, 768, True),
     (16, 2, 2, 256, 2, 512, True),
+    (16, 2, 2, 2048, 1, 4096, True),   # two column blocks of 1024 steps (k*V = 4)
+    (16, 4, 1, 1024, 1, 2048, False),
 ]
 
 
