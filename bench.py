@@ -6,9 +6,12 @@ Default workload: the 2048 x 2048 N(0,1) projection, L=16, k=2, V=1, T=256, d = 
 65536-entry shuffled Gaussian-quantile codebook.
 
 Prints one JSON line (rank 0).  Alongside the throughput it reports the forward
-kernel's roofline (VALU-bound: algorithmic VALU operations per state update over the
-chip's VALU issue rate, timed live with HIP events around the forward launch) and the
-CPU oracle timed on a bounded sample of the same workload on this host.
+kernel's roofline -- VALU-bound: algorithmic issue slots per state update (packed fp32
+counting one slot) over 256 CUs x 64 slots x 2.4 GHz, the launch timed live with HIP
+events on its stream -- and the CPU oracle timed on a bounded sample of the same
+workload on this host.  It also times the encode of the 4096 x 4096 weighted workload
+('weighted'), tcq_decode and the fused decode + GEMV on the encoded matrix, the
+pre-processing kernels, the soft trellis and the error-feedback driver.
 """
 from __future__ import annotations
 
@@ -25,35 +28,35 @@ sys.path.insert(0, ROOT)
 
 METRIC = "weights encoded/s (L=16,k=2,T=256 Viterbi) + % VALU peak ACS ops/s"
 
-# MI355X: 256 compute units of 4 SIMDs, 2.4 GHz peak engine clock.  A SIMD issues up to
-# two wave64 VALU instructions (from different waves) every 4 clocks: 128 VALU lane-ops
-# per clock per CU, non-packed.  This is the published fp32 vector rate (157.3 TFLOP/s)
-# with an FMA counted as one op instead of two.  (Not every instruction pairs: v_min3 and
-# other 3-source integer ops issue one per 4 clocks.)
+# MI355X: 256 compute units of 4 SIMDs (16 lanes each), 2.4 GHz peak engine clock.
 N_CU = 256
-LANES_PER_CU_CLK = 128
 CLOCK_HZ = 2.4e9
-VALU_PEAK_OPS = N_CU * LANES_PER_CU_CLK * CLOCK_HZ  # 7.86e13 lane-ops/s
 HBM_PEAK_GBPS = 8000.0
+# VALU issue-slot peak: 256 CUs x 64 lane-slots per clock x 2.4 GHz = 3.93e13 slots/s.  A
+# packed-fp32 instruction does two fp32 operations in one slot and an FMA counts as two
+# flops, so this is the published 157.3 TFLOP/s fp32 vector rate.
+VALU_SLOT_PEAK = N_CU * 64 * CLOCK_HZ
+# The same chip counted in non-packed lane operations issued two per SIMD per 4 clocks
+# (dual issue from different waves): 7.86e13 lane-ops/s.  Reported as a second view.
+VALU_DUAL_ISSUE_PEAK_OPS = 2 * VALU_SLOT_PEAK
+
+
+def slots_per_state_update(k: int, V: int) -> float:
+    """Algorithmic VALU issue slots per state update (one successor at one step), the
+    slot model the throughput target is stated in: the branch metric and add take 1.5 V
+    packed-fp32 slots (subtract, multiply by d and fused multiply-add per coordinate,
+    two lanes per packed slot), and the group compare-select 2 (G - 1) / G slots (G - 1
+    minima and G - 1 compares shared by the G = 2^(kV) successors of a group)."""
+    G = 2 ** (k * V)
+    return 1.5 * V + 2.0 * (G - 1) / G
 
 
 def valu_ops_per_state_update(k: int, V: int, weighted: bool) -> float:
-    """Algorithmic VALU lane-ops per state update (one successor at one step):
-    per coordinate a subtract, a multiply by d (weighted only) and a fused multiply-add;
-    per group of G = 2^(kV) predecessors a tournament of G-1 minima and G-1 compares
-    (for the lowest-index argmin), shared by the group's G successors."""
+    """The same work in non-packed lane operations: per coordinate a subtract, a multiply
+    by d (weighted only) and a fused multiply-add; per group the tournament of G - 1
+    minima and G - 1 compares.  The library is built without packed fp32."""
     G = 2 ** (k * V)
     return V * (3.0 if weighted else 2.0) + 2.0 * (G - 1) / G
-
-
-def packed_slot_model_pct(updates_per_s: float, k: int, V: int) -> float:
-    """The slot model the target is stated in: per state update 1.5 V packed-fp32 slots
-    for the branch metric and add, plus 2 (G - 1) / G for the group compare-select,
-    against 256 CUs x 64 slots per clock x 2.4 GHz (3.93e13 slots/s).  Reported next to
-    the roofline, which is against the dual-issue peak and counts non-packed operations."""
-    G = 2 ** (k * V)
-    slots = 1.5 * V + 2.0 * (G - 1) / G
-    return 100.0 * updates_per_s * slots / (N_CU * 64 * CLOCK_HZ)
 
 
 def parse():
@@ -67,6 +70,11 @@ def parse():
     ap.add_argument("--cpu-threads", type=int, default=0, help="0: min(16, cpu count)")
     ap.add_argument("--gemv-iters", type=int, default=200,
                     help="calls of the fused decode+GEMV timed after the encoder (0: skip)")
+    ap.add_argument("--decode-iters", type=int, default=50,
+                    help="calls of tcq_decode timed after the encoder (0: skip)")
+    ap.add_argument("--also", default="2",
+                    help="comma-separated workloads whose encode is also timed (3 or 5 "
+                         "steps each); workload 2 is reported as 'weighted'")
     ap.add_argument("--preprocess-iters", type=int, default=100,
                     help="timed calls of the Hadamard and scale-field kernels (0: skip)")
     ap.add_argument("--bcjr-tau", type=float, default=0.1,
@@ -237,7 +245,7 @@ def bcjr_bench(torch, _lib, w, Wt, dt_, Ct, tau, steps):
     rate = updates / (ms / 1e3)
     return {"tau": tau, "ms": ms, "weights_per_s": w.weights / (ms / 1e3),
             "state_updates_per_s_per_pass": rate, "valu_slots_per_state": slots,
-            "valu_pct": 100.0 * rate * slots / VALU_PEAK_OPS}
+            "valu_pct": 100.0 * rate * slots / VALU_DUAL_ISSUE_PEAK_OPS}
 
 
 def bcjr_slots_per_state(kv, V):
@@ -296,6 +304,115 @@ def preprocess_bench(torch, _lib, w, Wt, iters):
     return out
 
 
+def decode_bench(torch, _lib, w, enc, Ct, iters):
+    """tcq_decode of the whole encoded matrix into an M x N buffer.  Algorithmic bytes
+    (HBM): 4 B written per weight, plus the bitstream and start states read."""
+    out = torch.empty((w.M, w.N), dtype=torch.float32, device=Ct.device)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        _lib.tcq_decode(enc.bitstream.data_ptr(), enc.start_state.data_ptr(), Ct.data_ptr(),
+                        w.M, w.N, w.L, w.k, w.V, w.T, out.data_ptr(), w.N, stream.cuda_stream)
+
+    for _ in range(3):
+        call()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(iters):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / iters
+    nbytes = 4 * w.weights + (enc.bitstream.numel() + enc.start_state.numel()) * 4
+    gbps = nbytes / (us / 1e6) / 1e9
+    return {"us_per_call": us, "algorithmic_bytes": nbytes,
+            "bytes_per_weight": nbytes / w.weights, "achieved_GBps": gbps,
+            "frac_hbm": gbps / HBM_PEAK_GBPS, "weights_per_s": w.weights / (us / 1e6)}
+
+
+class EncodeRun:
+    """One workload's inputs resident on the GPU, its outputs and workspace, and a timed
+    loop of tcq_encode_timed calls (the forward launch bracketed by HIP events on the
+    launch stream)."""
+
+    def __init__(self, torch, _lib, api, wl, index, quiet):
+        self.torch, self._lib = torch, _lib
+        w = self.w = wl.WORKLOADS[index]
+        log(f"[bench] workload {w.name}: generating inputs", quiet)
+        self.W = wl.make_weights(w)
+        self.d = wl.make_d(w)
+        self.C = _lib.tcq_make_codebook(w.L, w.V, w.codebook_seed)
+        dev = torch.device("cuda:0")
+        self.Wt = torch.from_numpy(self.W).to(dev)
+        self.dt = None if self.d is None else torch.from_numpy(self.d).to(dev)
+        self.Ct = torch.from_numpy(self.C).to(dev)
+        nb = w.blocks
+        self.ws = api.Workspace(_lib.tcq_encode_workspace_bytes(w.M, w.N, w.L, w.k, w.V, w.T),
+                                dev)
+        self.out = api.Encoded(
+            bitstream=torch.empty((nb, api.nwords(w.k, w.T)), dtype=torch.int32, device=dev),
+            start_state=torch.empty(nb, dtype=torch.int32, device=dev),
+            cost=torch.empty(nb, dtype=torch.float32, device=dev), recon=None)
+
+    def step(self, e0=None, e1=None):
+        w, t = self.w, self.torch
+        self._lib.tcq_encode_timed(
+            self.Wt.data_ptr(), w.M, w.N, w.N, None if self.dt is None else self.dt.data_ptr(),
+            self.Ct.data_ptr(), w.L, w.k, w.V, w.T, self.out.bitstream.data_ptr(),
+            self.out.start_state.data_ptr(), self.out.cost.data_ptr(), None, w.N, self.ws.ptr,
+            self.ws.nbytes, t.cuda.current_stream().cuda_stream, e0, e1)
+
+    def timed(self, steps, warmup):
+        """(ms per step by the host clock, forward-launch ms of every timed step)."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:  # torch creates its events lazily, at the first record
+            a.record(stream)
+            b.record(stream)
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in ev:
+            self.step(a.cuda_event, b.cuda_event)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        return ms, [a.elapsed_time(b) for a, b in ev]
+
+    def summary(self, ms_per_step, acs):
+        """Throughput and the forward kernel's rates for one timed run."""
+        w = self.w
+        acs_ms = float(np.mean(acs))
+        updates = w.blocks * (w.T // w.V) * (1 << w.L)
+        rate = updates / (acs_ms / 1e3)
+        slots = slots_per_state_update(w.k, w.V)
+        ops = valu_ops_per_state_update(w.k, w.V, self.d is not None)
+        bp_bytes = w.blocks * (w.T // w.V) * (1 << (w.L - w.k * w.V)) * (w.k * w.V) / 8
+        # Every state update reads its successor's V codebook values (fp32) from the
+        # L2-resident codebook copies: this stream, not HBM, bounds the register-resident
+        # forward kernels in practice.
+        cb_bytes = updates * 4 * w.V
+        return {"workload": w.name, "ms_per_step": ms_per_step,
+                "weights_per_s": w.weights / (ms_per_step / 1e3),
+                "kernel_ms": acs_ms, "kernel_ms_each": acs,
+                "state_updates_per_launch": updates, "state_updates_per_s": rate,
+                "slots_per_update": slots,
+                "valu_pct_slot_model": 100.0 * rate * slots / VALU_SLOT_PEAK,
+                "valu_ops_per_update": ops,
+                "valu_pct_dual_issue_ops": 100.0 * rate * ops / VALU_DUAL_ISSUE_PEAK_OPS,
+                "bp_write_GBps": bp_bytes / (acs_ms / 1e3) / 1e9,
+                "bp_pct_hbm": 100.0 * bp_bytes / (acs_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                "codebook_l2_B_per_clk_per_cu": cb_bytes / (acs_ms / 1e3) / (N_CU * CLOCK_HZ),
+                "share_of_step": acs_ms / ms_per_step}
+
+    def free(self):
+        del self.Wt, self.dt, self.Ct, self.ws, self.out
+        self.torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -322,67 +439,20 @@ def main():
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n}))
         return
     _lib.load()  # fail loudly if the HIP library is missing
-    w = wl.WORKLOADS[args.workload]
-    log(f"[bench] workload {w.name}: generating inputs", args.quiet)
-    W = wl.make_weights(w)
-    d = wl.make_d(w)
-    C = _lib.tcq_make_codebook(w.L, w.V, w.codebook_seed)
-    dev = torch.device("cuda:0")
-    Wt = torch.from_numpy(W).to(dev)
-    dt_ = None if d is None else torch.from_numpy(d).to(dev)
-    Ct = torch.from_numpy(C).to(dev)
-    nb = w.blocks
-    ws_bytes = _lib.tcq_encode_workspace_bytes(w.M, w.N, w.L, w.k, w.V, w.T)
-    ws = api.Workspace(ws_bytes, dev)
-    out = api.Encoded(
-        bitstream=torch.empty((nb, api.nwords(w.k, w.T)), dtype=torch.int32, device=dev),
-        start_state=torch.empty(nb, dtype=torch.int32, device=dev),
-        cost=torch.empty(nb, dtype=torch.float32, device=dev), recon=None)
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for a, b in ev:  # torch creates its events lazily, at the first record
-        a.record(stream)
-        b.record(stream)
-
-    def step(i=None):
-        e0, e1 = (None, None) if i is None else (ev[i][0].cuda_event, ev[i][1].cuda_event)
-        _lib.tcq_encode_timed(Wt.data_ptr(), w.M, w.N, w.N,
-                              None if dt_ is None else dt_.data_ptr(), Ct.data_ptr(), w.L,
-                              w.k, w.V, w.T, out.bitstream.data_ptr(),
-                              out.start_state.data_ptr(), out.cost.data_ptr(), None, w.N,
-                              ws.ptr, ws.nbytes, stream.cuda_stream, e0, e1)
-
-    log(f"[bench] warmup {args.warmup}", args.quiet)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps", args.quiet)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    acs_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    weights_per_s = w.weights / (ms_per_step / 1e3)
-
-    updates_per_launch = nb * (w.T // w.V) * (1 << w.L)
-    ops = valu_ops_per_state_update(w.k, w.V, d is not None)
-    acs_ops_per_s = updates_per_launch / (acs_ms / 1e3)
-    achieved_tops = acs_ops_per_s * ops / 1e12
-    peak_tops = VALU_PEAK_OPS / 1e12
-    bp_bytes = nb * (w.T // w.V) * (1 << (w.L - w.k * w.V)) * (w.k * w.V) / 8
-    bp_gbps = bp_bytes / (acs_ms / 1e3) / 1e9
-    # Every state update reads its successor's V codebook values (fp32) from L2: the
-    # register-resident forward kernels stream 4 V bytes per update from the L2-resident
-    # codebook copies, and this stream, not HBM, is what bounds them in practice.
-    cb_bytes = updates_per_launch * 4 * w.V
-    cb_b_per_clk_cu = cb_bytes / (acs_ms / 1e3) / (N_CU * CLOCK_HZ)
+    run = EncodeRun(torch, _lib, api, wl, args.workload, args.quiet)
+    w = run.w
+    log(f"[bench] warmup {args.warmup}, timing {args.steps} steps", args.quiet)
+    ms_per_step, acs = run.timed(args.steps, args.warmup)
+    main_sum = run.summary(ms_per_step, acs)
+    acs_ms = main_sum["kernel_ms"]
+    # roofline of the forward kernel, in the slot model: algorithmic slots per state
+    # update x updates per launch / the launch's duration, against 3.93e13 slots/s
+    achieved = main_sum["state_updates_per_s"] * main_sum["slots_per_update"] / 1e12
+    peak = VALU_SLOT_PEAK / 1e12
 
     result = {
         "metric": METRIC,
-        "value": weights_per_s,
+        "value": main_sum["weights_per_s"],
         "unit": "weights/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -394,28 +464,44 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "L": w.L, "k": w.k, "V": w.V,
-                   "T": w.T, "d": "weighted (LDL diagonal)" if d is not None else "1 (NULL)",
+                   "T": w.T, "d": "weighted (LDL diagonal)" if run.d is not None else "1 (NULL)",
                    "codebook": f"2^{w.L} shuffled Gaussian quantiles, seed {w.codebook_seed}"},
-        "roofline": {"bound": "alu", "achieved": achieved_tops, "peak": peak_tops,
-                     "unit": "TOP/s", "frac": achieved_tops / peak_tops,
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak,
+                     "unit": "Tslot/s", "frac": achieved / peak,
+                     "model": "VALU issue slots: 1.5 V + 2 (G - 1) / G per state update "
+                              "(packed fp32 = 1 slot), peak 256 CU x 64 x 2.4 GHz",
                      "traffic": measured_traffic(w.name)},
-        "acs": {"kernel_ms": acs_ms, "state_updates_per_s": acs_ops_per_s,
-                "valu_ops_per_update": ops, "valu_pct": 100.0 * achieved_tops / peak_tops,
-                "valu_pct_packed_slot_model": packed_slot_model_pct(acs_ops_per_s, w.k, w.V),
-                "bp_write_GBps": bp_gbps, "bp_pct_hbm": 100.0 * bp_gbps / HBM_PEAK_GBPS,
-                "codebook_l2_bytes": cb_bytes, "codebook_l2_B_per_clk_per_cu": cb_b_per_clk_cu,
-                "share_of_step": acs_ms / ms_per_step},
+        "acs": main_sum,
     }
     if args.gemv_iters > 0:
         log(f"[bench] fused decode+GEMV on the encoded matrix, {args.gemv_iters} calls",
             args.quiet)
-        result["decode_gemv"] = gemv_bench(torch, _lib, w, out, Ct, args.gemv_iters)
+        result["decode_gemv"] = gemv_bench(torch, _lib, w, run.out, run.Ct, args.gemv_iters)
+    if args.decode_iters > 0:
+        log(f"[bench] decode of the encoded matrix, {args.decode_iters} calls", args.quiet)
+        result["decode"] = decode_bench(torch, _lib, w, run.out, run.Ct, args.decode_iters)
     if args.preprocess_iters > 0:
         log("[bench] pre-processing kernels", args.quiet)
-        result["preprocess"] = preprocess_bench(torch, _lib, w, Wt, args.preprocess_iters)
+        result["preprocess"] = preprocess_bench(torch, _lib, w, run.Wt, args.preprocess_iters)
     if args.bcjr_tau > 0:
         log(f"[bench] soft trellis at tau={args.bcjr_tau}", args.quiet)
-        result["bcjr"] = bcjr_bench(torch, _lib, w, Wt, dt_, Ct, args.bcjr_tau, 1)
+        result["bcjr"] = bcjr_bench(torch, _lib, w, run.Wt, run.dt, run.Ct, args.bcjr_tau, 1)
+    W, d, C = run.W, run.d, run.C
+    run.free()
+    others = [int(x) for x in args.also.split(",") if x.strip() != ""]
+    for idx in others:
+        if idx == args.workload:
+            continue
+        o = EncodeRun(torch, _lib, api, wl, idx, args.quiet)
+        steps = 3 if o.w.weights > 20e6 else 5
+        log(f"[bench] workload {o.w.name}: warmup 1, timing {steps} steps", args.quiet)
+        oms, oacs = o.timed(steps, 1)
+        entry = o.summary(oms, oacs)
+        entry["steps"] = steps
+        o.free()
+        result.setdefault("workloads", {})[o.w.name] = entry
+        if o.w.index == 2:
+            result["weighted"] = entry
     if args.ldlq_workload >= 0:
         log(f"[bench] error-feedback driver on workload {args.ldlq_workload}", args.quiet)
         result["ldlq"] = ldlq_bench(torch, _lib, wl, args.ldlq_workload, args.ldlq_steps)

@@ -15,14 +15,17 @@
  *   state s_0 < 2^(L-kV) is chosen freely per block.  The encoder returns, per block,
  *   the path of minimum cost
  *       J = sum_i d_i (w_i - what_i)^2
- *   found by the Viterbi algorithm (the cheapest path into every state is kept).
+ *   found by Viterbi dynamic programming (each state retains its lowest-cost incoming
+ *   path after every step).
  *
  * Arithmetic: fp32 throughout.  Each weight contributes, in order,
  *       e = fl(w - c);  acc = fmaf(fl(d * e), e, acc)        (d == NULL: fmaf(e, e, acc))
  * starting from acc = +0; at each step the predecessor kept for a state is the one
  * with the smallest cost, the lowest predecessor index j on ties, where the
  * predecessors of s' are (j << (L-kV)) | (s' >> kV), j = 0 .. 2^kV - 1.  The chosen end
- * state is the lowest-index minimum.  Costs are never renormalised.
+ * state is the lowest-index minimum.  Costs are never renormalised.  A square that
+ * overflows fp32 makes a cost +inf, which is compared like any other value (equal costs
+ * keep the lowest index), so such a block still yields a valid path of cost +inf.
  *
  * Memory: every pointer argument of tcq_encode / tcq_decode is a DEVICE pointer owned
  * by the caller (for instance torch tensors); the library never frees or retains them.

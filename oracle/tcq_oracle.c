@@ -9,15 +9,17 @@
  *    (QTIP abstract, "QTIP: Quantization with Trellises and Incoherence Processing").
  *    Reading used here: an L-bit state takes in k*V fresh bits per step,
  *    s_t = ((s_{t-1} << kV) | b_t) mod 2^L, and emits the V values in codebook row s_t.
- *  - The state picks the allowed subset of values, the written bits pick a value inside
- *    it and also set the next state (Pingala-8 post, the trellis-coded quantization
- *    paragraph and its 1-bit toy example).
+ *  - Each state restricts the next group to one coset of the codebook; the chunk of
+ *    bits coded for the group both indexes a value of that coset and determines the
+ *    following state (Pingala-8 post, the trellis-coded quantization paragraph and its
+ *    1-bit toy example).
  *  - The cost is a sum of squared errors (same toy: plain rounding totals 1.42).
  *  - Each squared error is weighted by d_i, the diagonal of the Hessian's LDL factor,
  *    inside the Viterbi branch metric, and each coding block carries its own start
  *    state (CurveTQ abstract on the aqora listing).
- *  - The search is the Viterbi algorithm: dynamic programming keeping the cheapest path
- *    into every state (Pingala-8 post, paragraph after the toy).
+ *  - The optimum over all paths comes from Viterbi dynamic programming: after each step
+ *    a state retains only its lowest-cost incoming path (Pingala-8 post, the paragraph
+ *    that follows the toy).
  *  - The codebook is a closed-form quantile table (CurveTQ abstract): Gaussian quantiles
  *    Phi^-1((j+1/2)/N), placed in a seeded shuffled order.
  *
@@ -495,10 +497,10 @@ int oracle_ldlq_row(const float *w, const float *U, long ldu, const float *d, co
 
 /* ------------------------------------------------------------------------- */
 /* Soft trellis (BCJR) at temperature tau.                                     */
-/* BCJR-QAT abstract on the aqora listing: replace the Viterbi argmax by the   */
-/* BCJR forward-backward sum-product at a temperature, giving a soft codeword  */
-/* equal to the Boltzmann expectation over trellis paths, which tends to the   */
-/* hard code as the temperature goes to 0.  Reading: every path of the block   */
+/* BCJR-QAT abstract on the aqora listing: a tempered forward-backward (BCJR) */
+/* pass takes the place of the hard minimum; its output is the mean emitted    */
+/* value under a Gibbs distribution over paths, and as the temperature falls   */
+/* to zero it returns to the Viterbi code.  Reading: every path of the block   */
 /* (free start: s_1 may be any of the 2^L states) has energy J, the same       */
 /* weighted squared error the Viterbi search minimises, and probability        */
 /* exp(-J / tau) / Z.  The soft codeword of weight (t-1)V+v is the expectation */

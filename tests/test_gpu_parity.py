@@ -207,3 +207,37 @@ def test_exact_ties(oracle_lib, L, k, V, T, M, N, split_min, weighted):
         assert int(s0[b]) < (1 << (L - k * V))
         g_path = oracle_lib.path_cost(wb, db, C, L, k, V, T, bits[b], int(s0[b]))
         assert g_path.view(np.uint32) == oc[b].view(np.uint32)
+
+
+# A block whose first weight is 1e20: its squares overflow, every path of the block costs
+# +inf, and every comparison of the search is between equal costs.  The lowest-index rule
+# then keeps the all-zero path (pinned by brute force in test_oracle_bruteforce.py), which
+# every kernel family must return: the generic kernel with costs in LDS (L <= 13) or in
+# the workspace (L = 14), and the L = 16 register kernels for k*V = 2, 3 and 4.  The
+# other blocks of each matrix are ordinary.
+OVERFLOW_CASES = [
+    # L, k, V, T, M, N
+    (8, 2, 1, 64, 2, 128),
+    (14, 2, 1, 32, 2, 64),
+    (16, 2, 1, 256, 2, 512),
+    (16, 3, 1, 256, 2, 512),
+    (16, 2, 2, 256, 2, 512),
+]
+
+
+@pytest.mark.parametrize("L,k,V,T,M,N", OVERFLOW_CASES)
+@pytest.mark.parametrize("weighted", [False, True])
+def test_overflowed_costs(oracle_lib, L, k, V, T, M, N, weighted):
+    _say(f"overflow L={L} k={k} V={V} T={T} weighted={weighted}")
+    W, d = wl.random_small(4242 + L + k, M, N, weighted)
+    W[1, T] = np.float32(1e20)  # first weight of block N/T + 1
+    C = oracle_lib.make_codebook(L, V, 23)
+    bits, s0, cost, recon = _gpu_encode(W, d, C, L, k, V, T, recon=True)
+    nb = M * (N // T)
+    rep = parity.compare(oracle_lib, W, d, C, L, k, V, T, np.arange(nb), bits, s0, cost,
+                         threads=THREADS)
+    assert rep.ok() and rep.exact == nb, str(rep)
+    b = N // T + 1
+    assert np.isinf(cost[b]) and s0[b] == 0 and not bits[b].any()
+    assert np.all(np.isfinite(np.delete(cost, b)))
+    assert np.all(recon[1, T:2 * T] == C[0, :].reshape(-1)[np.arange(T) % V])

@@ -131,3 +131,37 @@ def test_oracle_fixed_start(oracle_lib, L, k, V, T):
         fixed.append(cost)
     # a free start is the best of all fixed starts
     assert free_cost == min(fixed)
+
+
+@pytest.mark.parametrize("L,k,V,T", [(4, 1, 1, 5), (5, 2, 1, 4), (6, 2, 2, 4), (6, 3, 1, 3)])
+def test_oracle_overflowed_costs(oracle_lib, L, k, V, T):
+    """A weight of 1e20 squares past the fp32 range, so every path costs +inf.
+    With it first, every comparison of the search is between equal (+inf) costs, so the
+    optimum with the smallest tie key -- the all-zero path: end state 0, predecessor 0 at
+    every step -- is what the lowest-index rule must return.  With it second, the step-2
+    choices still compare finite prefixes; the end state must still be state 0 (the
+    lowest index among equal final costs) and the path a valid one of cost +inf."""
+    rng = np.random.default_rng(31 + L + T)
+    w, d, C = _random_problem(rng, L, k, V, T, True, "quantile")
+    w0 = w.copy()
+    w0[0] = np.float32(1e20)
+    bits, s0, cost = oracle_lib.encode_block(w0, d, C, L, k, V, T)
+    best, _, bbits, bs0, costs, _ = bf.best_path(w0, d, C, L, k, V, T)
+    assert np.all(np.isinf(costs)) and np.isinf(best) and np.isinf(cost)
+    assert s0 == bs0 == 0 and np.array_equal(bits, bbits) and not bits.any()
+    w1 = w.copy()
+    w1[V] = np.float32(1e20)
+    bits, s0, cost = oracle_lib.encode_block(w1, d, C, L, k, V, T)
+    assert np.isinf(cost) and s0 < (1 << (L - k * V))
+    last_chunk_bits = k * V
+    tail = T // V * k * V  # bits in the stream
+    assert bf_last_chunk(bits, tail, last_chunk_bits) == 0
+    assert np.isinf(oracle_lib.path_cost(w1, d, C, L, k, V, T, bits, s0))
+
+
+def bf_last_chunk(bits, nbits, kv):
+    """Value of the last kv-bit chunk of an MSB-first packed stream of nbits bits."""
+    v = 0
+    for pos in range(nbits - kv, nbits):
+        v = (v << 1) | ((int(bits[pos // 32]) >> (31 - pos % 32)) & 1)
+    return v

@@ -1,10 +1,11 @@
 """The oracle against the worked example printed on the pages.
 
-Pingala-8 blog post, the 1-bit toy trellis: four levels in two cosets, state 0 may use
-{-1.5, 0.5} and state 1 {-0.5, 1.5}; bit 0 picks the lower value, bit 1 the higher,
-and the bit written becomes the next state; start in state 0 and encode
-[-0.4, 0.1, 1.5].  The page prints the plain 1-bit rounding score, 1.42, and says
-greedy trellis rounding loses to it while the searched path beats it.
+Pingala-8 blog post, the 1-bit toy trellis.  Data of the example: the cosets
+{-1.5, 0.5} (state 0) and {-0.5, 1.5} (state 1), the weights [-0.4, 0.1, 1.5] and the
+start state 0.  Its rule, restated: the coded bit selects the smaller (0) or larger (1)
+member of the current coset, and that same bit is the state for the next weight.  The
+page gives 1.42 as the score of plain 1-bit rounding, and orders the methods: greedy
+coding along the trellis scores worse than 1.42, the Viterbi search better.
 """
 import json
 import os

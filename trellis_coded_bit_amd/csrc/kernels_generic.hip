@@ -2,8 +2,8 @@
 // groups of states across threads, cost vectors double-buffered in LDS (L <= 13) or in
 // the workspace (larger L, L2-resident per block), backpointers as bit-planes.
 //
-// The step (Pingala-8 post, Viterbi paragraph: keep the cheapest path into every
-// state; bitshift structure from the QTIP abstract; weighted metric from the CurveTQ
+// The step (Pingala-8 post, Viterbi paragraph: each state retains its lowest-cost
+// incoming path; bitshift structure from the QTIP abstract; weighted metric from the CurveTQ
 // abstract): the predecessors of s' = (x << kv) | b are (j << (L-kv)) | x, so one
 // min/argmin per group x serves its 2^kv successors.  Starting every state at cost +0
 // before step 1 is the free start: step 1 then extends +0 by the branch metric, and
@@ -101,12 +101,15 @@ __global__ __launch_bounds__(kThreads) void acs_generic_kernel(
         Jn = tmp;
     }
 
-    // lowest-index minimum over the final cost vector
+    // lowest-index minimum over the final cost vector.  A thread's first state is taken
+    // unconditionally, so a vector of +inf costs (squares that overflowed) still selects
+    // a real state -- the lowest one, as the reduction below breaks ties by index --
+    // and never leaves the 0xFFFFFFFF marker of threads that own no state.
     float bv = __builtin_inff();
     uint32_t bi = 0xFFFFFFFFu;
     for (int64_t s = tid; s < nstates; s += kThreads) {
         const float v = J[s];
-        if (v < bv) {
+        if (bi == 0xFFFFFFFFu || v < bv) {
             bv = v;
             bi = static_cast<uint32_t>(s);
         }
