@@ -177,6 +177,45 @@ def gemv_bench(torch, _lib, w, enc, Ct, iters):
             "frac_hbm": gbps / HBM_PEAK_GBPS, "weights_per_s": w.weights / (us / 1e6)}
 
 
+def gemv_shapes_bench(torch, _lib, iters):
+    """The fused decode + GEMV on the two 8B-class MLP shapes (14336 x 4096 at k = 2,
+    V = 2 and 4096 x 14336 at k = 3), on seeded random bitstreams (every stream with
+    s_0 < 2^(L-kV) is a trellis path; the decode work does not depend on the path)."""
+    out = []
+    for M, N, L, k, V, T in ((14336, 4096, 16, 2, 2, 256), (4096, 14336, 16, 3, 1, 256)):
+        g = torch.Generator(device="cpu").manual_seed(M + N + k)
+        nb = M * (N // T)
+        nw = (k * T + 31) // 32
+        bits = torch.randint(-2 ** 31, 2 ** 31 - 1, (nb, nw), generator=g,
+                             dtype=torch.int32).cuda()
+        s0 = torch.randint(0, 1 << (L - k * V), (nb,), generator=g, dtype=torch.int32).cuda()
+        C = torch.from_numpy(_lib.tcq_make_codebook(L, V, 3001)).cuda()
+        x = torch.randn(N, generator=g).cuda()
+        y = torch.empty(M, dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def call():
+            _lib.tcq_decode_gemv(bits.data_ptr(), s0.data_ptr(), C.data_ptr(), M, N, L, k, V,
+                                 T, x.data_ptr(), y.data_ptr(), stream.cuda_stream)
+
+        for _ in range(3):
+            call()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / iters
+        nbytes = (bits.numel() + s0.numel() + N + M) * 4
+        gbps = nbytes / (us / 1e6) / 1e9
+        out.append({"shape": f"{M}x{N} L={L} k={k} V={V} T={T}", "us_per_call": us,
+                    "algorithmic_bytes": nbytes, "achieved_GBps": gbps,
+                    "frac_hbm": gbps / HBM_PEAK_GBPS, "weights_per_s": M * N / (us / 1e6)})
+    return out
+
+
 def ldlq_bench(torch, _lib, wl, index, steps):
     """The error-feedback driver over a whole weighted workload: N/T encodes in sequence
     with the feedback updates between them.  Inputs (W, the block factor U of the
@@ -477,6 +516,9 @@ def main():
         log(f"[bench] fused decode+GEMV on the encoded matrix, {args.gemv_iters} calls",
             args.quiet)
         result["decode_gemv"] = gemv_bench(torch, _lib, w, run.out, run.Ct, args.gemv_iters)
+    if args.gemv_iters > 0:
+        log("[bench] fused decode+GEMV on the 8B-class MLP shapes", args.quiet)
+        result["decode_gemv_shapes"] = gemv_shapes_bench(torch, _lib, max(10, args.gemv_iters // 2))
     if args.decode_iters > 0:
         log(f"[bench] decode of the encoded matrix, {args.decode_iters} calls", args.quiet)
         result["decode"] = decode_bench(torch, _lib, w, run.out, run.Ct, args.decode_iters)

@@ -109,19 +109,26 @@ def test_hadamard_full_size_sampled_rows(oracle_lib):
     assert np.allclose(np.linalg.norm(Yc, axis=1), np.linalg.norm(W, axis=1), rtol=1e-4)
 
 
+def _scale_bounds(M, N):
+    """(a, b) relative bounds from the kernels' summation order."""
+    return (N / 256 + 16) * U32, (M / 64 + 64 + N / 256 + 32) * U32
+
+
 def _check_scale(W, a, b, Wn, rows):
     import oracle
     M, N = W.shape
     ra, rb, rWn = oracle.scale_field(W)
-    ta = (N / 256 + 16) * U32
-    tb = (M / 64 + 64 + N / 256 + 32) * U32
+    ta, tb = _scale_bounds(M, N)
+    _say(f"  a: worst {np.max(np.abs(a - ra) / ra) / ta:.3g} of the bound; "
+         f"b: worst {np.max(np.abs(b - rb) / rb) / tb:.3g} of the bound")
     assert np.all(np.abs(a - ra) <= ta * ra)
     assert np.all(np.abs(b - rb) <= tb * rb)
     tw = (ta / U32 + tb / U32 + 4) * U32
     assert np.all(np.abs(Wn[rows] - rWn[rows]) <= tw * np.abs(rWn[rows]) + 1e-37)
 
 
-@pytest.mark.parametrize("M,N", [(1, 1), (3, 17), (64, 300), (130, 1000), (257, 64)])
+@pytest.mark.parametrize("M,N", [(1, 1), (3, 17), (64, 300), (130, 1000), (257, 64),
+                                 (33, 1024), (17, 4100), (40, 8192), (9, 14336), (5, 16384)])
 def test_scale_field_parity(oracle_lib, M, N):
     _say(f"scale field M={M} N={N}")
     rng = np.random.default_rng(M * 1000 + N)

@@ -2,7 +2,7 @@
 2 <= L <= 16, k*V < L, k*V <= 8, V in {1, 2, 4}, strided rows, Gaussian / heavy-tailed /
 dyadic (tie-rich) weights, weighted and unweighted, quantile and random codebooks.
 Per case: encode with reconstruction (parity rule of tests/parity.py, reconstruction
-bitwise equal to the oracle's decode), decode-GEMV (error bound of test_gpu_gemv.py) and,
+bitwise equal to the oracle's decode), decode-GEMV (error bound of gemv_check.py) and,
 where the float64 oracle is quick (L <= 12, k*V <= 4), the soft trellis (bounds of
 test_gpu_bcjr.py)."""
 import sys
@@ -99,7 +99,7 @@ def test_random_case(oracle_lib, case):
     x = rng.standard_normal(N).astype(np.float32)
     y = tg._gpu_gemv(bits, s0, C, x, M, N, L, k, V, T)
     yref, What = oracle.decode_gemv(bits, s0, C, x, M, N, L, k, V, T)
-    tg._check(y, yref, What, x, N)
+    tg._check(y, yref, What, x, M, N, L, k, V, T)
     if k * V <= 4 and L <= 12 and kind != 2:
         tau = float(rng.choice([0.05, 0.3, 2.0]))
         soft, logz = tb._gpu(Wn, d, C, L, k, V, T, tau)

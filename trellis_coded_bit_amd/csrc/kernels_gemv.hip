@@ -4,15 +4,13 @@
 //
 // The state of step t is the L-bit window of s_0 || b_1 || ... || b_n that ends with
 // chunk b_t, so it can be read straight from two neighbouring 32-bit words of the stream
-// (the word before the first one being s_0).  A lane owns one stream word and decodes
-// every step whose chunk ends inside it.
+// (the word before the first one being s_0).
 //
 // The codebook (2^L x V floats; 256 KiB at L=16, V=1) is read at random, one entry per
 // step.  From L2 every such read pulls a whole cache line into L1, so the table is staged
-// through LDS instead, up to 128 KiB at a time: P = table / part passes over the stream,
-// each adding the products whose state falls in the part held in LDS.  Each wave keeps
-// the same rows in every pass and adds its part sums to y in pass order, so results are
-// deterministic.
+// through LDS instead, 128 KiB at a time: P = table / part passes, each adding the
+// products whose state falls in the part held in LDS.  Results are deterministic: every
+// row is summed in a fixed order (stated with each kernel).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -26,8 +24,7 @@ namespace {
 constexpr int kGemvThreads = 1024;
 constexpr int kGemvWaves = kGemvThreads / 64;  // rows in flight per workgroup
 constexpr int64_t kGemvPartBytes = 128 << 10;     // largest codebook part in LDS
-constexpr int64_t kGemvMinPartBytes = 32 << 10;   // smallest part worth staging x for
-constexpr int64_t kGemvLdsBytes = 152 << 10;      // dynamic LDS used at most
+constexpr int64_t kGemvLdsBytes = 132 << 10;      // dynamic LDS used at most
 
 struct GemvArgs {
     const uint32_t *bits;
@@ -44,136 +41,312 @@ struct GemvArgs {
     int parts;
     int64_t step_c;     // 64 / nwords: blocks advanced per 64 words
     int step_j;         // 64 % nwords
-    int64_t xt_len;     // floats of x staged in LDS (tiled kernel)
 };
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
-// Tiled kernel.  A unit is U = KV / gcd(KV, 32) stream words holding exactly S = 32 U / KV
-// whole steps; every block's stream is a whole number of units, so step q of row unit u
-// is step g = u S + q of the row and multiplies x[g V + v].  x is staged once per
-// workgroup in LDS in the order [tile of 64 units][q][lane][v], which makes the reads of
-// a wave for one q contiguous.  R waves share a row (R = 1 unless the rows are too few
-// to give every CU a workgroup): wave r of the group takes the row's tiles of 64 units
-// r, r + R, ..., lane l owning the l-th unit of each; the 64 lane sums meet in a shuffle
-// tree, and the R wave sums are added in order through LDS.  A step whose state is in
-// another codebook part multiplies an exact 0 (its table read is masked off), which
-// leaves the sum unchanged.
-template <int KV, int V, int R>
-__global__ __launch_bounds__(kGemvThreads) void gemv_tiled_kernel(GemvArgs a) {
-    static_assert(R == 1 || R == 2 || R == 4, "waves per row");
-    extern __shared__ float lds[];
-    constexpr int U = KV / gcd_c(KV, 32);
-    constexpr int S = 32 * U / KV;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int64_t per_part = int64_t{1} << a.part_log2;
-    float *tab = lds;
-    float *xt = lds + per_part * V;
-    const int64_t upr = a.wpr / U;          // units per row
-    const int upb = a.nwords / U;           // units per block
-    for (int64_t j = tid; j < a.xt_len; j += kGemvThreads) {
-        const int v = static_cast<int>(j % V);
-        const int64_t r = j / V;
-        const int l = static_cast<int>(r & 63);
-        const int64_t tq = r >> 6;
-        const int q = static_cast<int>(tq % S);
-        const int64_t u = (tq / S) * 64 + l;
-        xt[j] = (u < upr) ? a.x[(u * S + q) * V + v] : 0.0f;
-    }
-    const int wv = tid >> 6;
-    const int rsub = wv & (R - 1);            // this wave's share of its row's tiles
-    constexpr int kRowsPerWg = kGemvWaves / R;
-    const uint32_t mask = (1u << a.L) - 1u;
-    const uint32_t pmask = static_cast<uint32_t>(per_part - 1);
-    const int plog = a.part_log2;
-    const int64_t step_c = 64 / upb;
-    const int step_j = 64 % upb;
-    for (int p = 0; p < a.parts; ++p) {
-        __syncthreads();  // previous pass finished with the table
-        if ((reinterpret_cast<uintptr_t>(a.C) & 15) == 0 && per_part * V >= 4) {
-            const float4 *src = reinterpret_cast<const float4 *>(a.C + p * per_part * V);
-            float4 *dst = reinterpret_cast<float4 *>(tab);
-            for (int64_t i = tid; i < per_part * V / 4; i += kGemvThreads) dst[i] = src[i];
-        } else {
-            const float *srcf = a.C + p * per_part * V;
-            for (int64_t i = tid; i < per_part * V; i += kGemvThreads) tab[i] = srcf[i];
+// Column kernel.  A unit is U = KV / gcd(KV, 32) stream words holding exactly S = 32 U / KV
+// whole steps, and every block's stream is a whole number of units, so unit u of a row
+// covers the row's steps u S .. u S + S - 1 (columns (u S + q) V + v).  A workgroup of
+// 1024 threads is R_G row groups of NT column threads (NT a multiple of 64, R_G = 1024 /
+// NT); column thread c owns units c, c + NT, ... (G of them; G = 1 is built, so rows
+// of at most 1024 units) in every row, so its G S V values of x are loaded into
+// registers once.  The workgroup takes a contiguous range of
+// rows; row group r takes rows r, r + R_G, ... of it, up to RT at a time (a tile).  For
+// each unit of a tile row the thread keeps the unit's words w_1..w_U and the words
+// m_j = w_j[15:0] w_{j+1}[31:16] that straddle them (w_0 is the word before the unit, or
+// s_0 for a block's first unit): every L-bit state window (L <= 16) then lies inside one
+// of these registers and is one bit-field extract.  For each part of the codebook in LDS
+// (P passes per tile) the state becomes an LDS offset that points at the step's table row
+// when the state lies in the part and at a row of zeros past the part otherwise -- an
+// unsigned clamp, no branch -- so each step adds an exact 0 in every pass but one.
+// Summation order of row y[r]: each column thread keeps one fp32 chain, fmaf over passes,
+// its units, steps and coordinates in that order (at most G S V nonzero terms); the 64
+// chains of a wave meet in a 6-level DPP reduction; the NT / 64 wave sums of the row are
+// added in wave order.
+constexpr int kColThreads = 1024;
+constexpr int kColWaves = kColThreads / 64;
+constexpr int kColRowsMax = 12;   // rows of a tile, per thread, at most
+constexpr int kColRegBudget = 66;  // registers for x, a tile's stream words and sums
+constexpr int kColBatch = 8;       // table gathers in flight per thread
+constexpr int kColTabFloats = static_cast<int>(kGemvPartBytes / 4);  // largest part
+
+struct ColArgs {
+    const uint32_t *bits;
+    const uint32_t *s0;
+    const float *C;
+    const float *x;
+    float *y;
+    int64_t M;
+    int64_t bpr;          // blocks per row
+    int nwords;           // stream words per block
+    int upb;              // units per block
+    int64_t upr;          // units per row
+    int L;
+    int nt;               // column threads per row group (multiple of 64)
+    int rgroups;          // row groups per workgroup
+    int rt;               // rows per row group in one tile (<= the kernel's RT)
+    int64_t rows_per_wg;  // contiguous rows of one workgroup
+    int part_log2;        // log2(states per codebook part)
+    int parts;
+    int c_aligned;        // C is 16-byte aligned and a part is whole float4s
+};
+
+template <int KV, int V, int G>
+struct ColShape {
+    static constexpr int U = KV / gcd_c(KV, 32);
+    static constexpr int S = 32 * U / KV;
+    static constexpr int NR = 2 * U;  // registers per unit: m_0, w_1, ..., m_{U-1}, w_U
+    // table gathers in flight per thread (fewer for rows of two or four floats)
+    static constexpr int kB = kColBatch / V;
+    static constexpr int B = kB < S ? kB : S;
+    // registers left for a tile's stream words and sums (one per row), by the budget
+    // measured to compile without spills at 128 VGPRs
+    static constexpr int kBudget = U == 1 ? kColRegBudget : kColRegBudget + 6;
+    static constexpr int kLeft =
+        kBudget - G * S * V - (G * S * V >= 32 && V > 1 ? 16 : 0) - B * V;
+    static constexpr int kFit = kLeft / (G * NR + 1);
+    // (three-word units keep 32 x values and six stream registers per row: fewer rows)
+    static constexpr int kCap = U == 1 ? kColRowsMax : kColRowsMax / 2;
+    static constexpr int RT = kFit < 1 ? 1 : (kFit > kCap ? kCap : kFit);
+};
+
+// Sum over the 64 lanes of a wave, returned in every lane: a scan within each row of 16
+// lanes (DPP row shifts by 1, 2, 4, 8), then row 0 into row 1 and row 2 into row 3, then
+// rows 0-1 into rows 2-3 (row broadcasts); lane 63 ends with the total.  Every lane's
+// value passes through at most 6 additions.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_term(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_term<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_term<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_term<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_term<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_term<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_term<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// log2 of the bytes of one table row
+template <int V>
+constexpr int log2_row_bytes() { return V == 1 ? 2 : (V == 2 ? 3 : 4); }
+
+// Part p of the table into LDS, then the row of zeros after it.  With 16-byte aligned
+// parts of at most 8 x 1024 float4, each thread issues its eight loads (the index clamped,
+// so every load is in bounds) before storing them.
+template <int V>
+__device__ __forceinline__ void col_copy_part(float *tab, bool vec, const float *C, int p,
+                                              int64_t nfl, int64_t n4, int tid) {
+    if (vec) {
+        const float4 *s4 = reinterpret_cast<const float4 *>(C + static_cast<int64_t>(p) * nfl);
+        float4 *d4 = reinterpret_cast<float4 *>(tab);
+        float4 t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t j = static_cast<int64_t>(u) * kColThreads + tid;
+            t[u] = s4[j < n4 ? j : n4 - 1];
         }
-        __syncthreads();
-        // the same number of row iterations in every wave of the workgroup (with R > 1
-        // there are barriers at the end of each)
-        for (int64_t base = static_cast<int64_t>(blockIdx.x) * kRowsPerWg; base < a.M;
-             base += static_cast<int64_t>(gridDim.x) * kRowsPerWg) {
-            const int64_t row = base + wv / R;
-            float acc = 0.0f;
-            const int u1 = rsub * 64 + lane;             // this lane's unit in its first tile
-            int64_t c = u1 / upb;                        // block of this lane's unit
-            int ju = u1 - static_cast<int>(c) * upb;     // unit within the block
-            for (int64_t u0 = rsub * 64; row < a.M && u0 < upr; u0 += 64 * R) {
-                if (u0 + lane < upr) {
-                    const int64_t blk = row * a.bpr + c;
-                    const uint32_t *wb = a.bits + blk * a.nwords + ju * U;
-                    uint32_t wd[U + 1];
-                    wd[0] = ju ? wb[-1] : a.s0[blk];
 #pragma unroll
-                    for (int i = 0; i < U; ++i) wd[i + 1] = wb[i];
-                    const float *xq = xt + (static_cast<int>(u0 >> 6) * S * 64 + lane) * V;
-                    // gather this unit's table entries (masked to the part in LDS), then
-                    // the products in step order
-                    float cv[S][V];
+        for (int u = 0; u < 8; ++u) {
+            const int64_t j = static_cast<int64_t>(u) * kColThreads + tid;
+            if (j < n4) d4[j] = t[u];
+        }
+    } else {
+        const float *src = C + static_cast<int64_t>(p) * nfl;
+        for (int64_t j = tid; j < nfl; j += kColThreads) tab[j] = src[j];
+    }
+    if (tid < 4) tab[nfl + tid] = 0.0f;
+}
+
+// One table row (V floats) from LDS; rows are V * 4 bytes and V * 4-byte aligned.
+template <int V>
+__device__ __forceinline__ void load_row(float (&c)[V], const char *p) {
+    if constexpr (V == 1) {
+        c[0] = *reinterpret_cast<const float *>(p);
+    } else if constexpr (V == 2) {
+        const float2 t = *reinterpret_cast<const float2 *>(p);
+        c[0] = t.x;
+        c[1] = t.y;
+    } else {
+        const float4 t = *reinterpret_cast<const float4 *>(p);
+        c[0] = t.x;
+        c[1] = t.y;
+        c[2] = t.z;
+        c[3] = t.w;
+    }
+}
+
+template <int KV, int V, int G>
+__global__ __launch_bounds__(kColThreads) void gemv_cols_kernel(ColArgs a) {
+    using Sh = ColShape<KV, V, G>;
+    constexpr int U = Sh::U, S = Sh::S, RT = Sh::RT, NR = Sh::NR;
+    constexpr int kLog = log2_row_bytes<V>();
+    // LDS: the table part at offset 0 (so a table offset is an LDS address), one row of
+    // zeros after it, then the wave sums of a tile's rows
+    __shared__ float tab[kColTabFloats + 4 + kColRowsMax * kColWaves];
+    const int tid = threadIdx.x;
+    const int rg = tid / a.nt;     // row group (uniform per wave: nt is a multiple of 64)
+    const int tc = tid - rg * a.nt;
+    const int wv = tid >> 6;
+    const int lane = tid & 63;
+    const bool active_rg = rg < a.rgroups;
+    const int64_t per_part = int64_t{1} << a.part_log2;
+    const uint32_t dummy = static_cast<uint32_t>(per_part) << kLog;  // the row of zeros
+    const int64_t nfl = per_part * V;                                // floats per part
+    const int64_t n4 = nfl / 4;
+    float(*red)[kColWaves] = reinterpret_cast<float(*)[kColWaves]>(tab + kColTabFloats + 4);
+
+    // x of this thread's units, in registers: x is first copied into LDS with coalesced
+    // loads (a row holds at most 1024 units of S V values: at most 32768 floats, which fit
+    // where the table parts go), then each thread reads its own S V values from there
+    const int64_t xlen = a.upr * S * V;
+    for (int64_t j = tid; j < xlen; j += kColThreads) tab[j] = a.x[j];
+    __syncthreads();
+    float xr[G][S][V];
 #pragma unroll
-                    for (int q = 0; q < S; ++q) {
-                        const int e = (q + 1) * KV;          // window end, bits into the unit
-                        const int jj = (e - 1) >> 5;         // word holding bit e - 1
-                        const uint32_t st =
-                            __builtin_amdgcn_alignbit(wd[jj], wd[jj + 1], 32 * (jj + 1) - e) & mask;
+    for (int g = 0; g < G; ++g) {
+        const int64_t u = tc + static_cast<int64_t>(g) * a.nt;
 #pragma unroll
-                        for (int v = 0; v < V; ++v) cv[q][v] = 0.0f;
-                        if ((st >> plog) == static_cast<uint32_t>(p)) {
-                            const float *cs = tab + (st & pmask) * V;
+        for (int q = 0; q < S; ++q)
 #pragma unroll
-                            for (int v = 0; v < V; ++v) cv[q][v] = cs[v];
-                        }
-                    }
+            for (int v = 0; v < V; ++v)
+                xr[g][q][v] = (active_rg && u < a.upr) ? tab[(u * S + q) * V + v] : 0.0f;
+    }
+
+    const bool vec = a.c_aligned && n4 <= 8 * kColThreads;
+
+    // where this thread's units sit in a row: block, unit within the block, word offset
+    const int64_t wpr = a.bpr * a.nwords;  // stream words per row
+    int64_t ublk[G], woff[G];
+    int ju[G];
+    bool uok[G];
 #pragma unroll
-                    for (int q = 0; q < S; ++q) {
+    for (int g = 0; g < G; ++g) {
+        const int64_t u = tc + static_cast<int64_t>(g) * a.nt;
+        uok[g] = u < a.upr;
+        ublk[g] = u / a.upb;
+        ju[g] = static_cast<int>(u - ublk[g] * a.upb);
+        woff[g] = ublk[g] * a.nwords + static_cast<int64_t>(ju[g]) * U;
+    }
+
+    const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * a.rows_per_wg;
+    int64_t r_end = r_begin + a.rows_per_wg;
+    if (r_end > a.M) r_end = a.M;
+    const int64_t tile_rows = static_cast<int64_t>(a.rgroups) * a.rt;
+    for (int64_t t0 = r_begin; t0 < r_end; t0 += tile_rows) {
+        // stream registers of the tile
+        uint32_t wr[RT][G][NR];
+        float acc[RT];
 #pragma unroll
-                        for (int v = 0; v < V; ++v)
-                            acc = __builtin_fmaf(cv[q][v], xq[q * 64 * V + v], acc);
-                    }
+        for (int i = 0; i < RT; ++i) {
+            acc[i] = 0.0f;
+            const int64_t row = t0 + rg + static_cast<int64_t>(a.rgroups) * i;
+            const bool rok = active_rg && i < a.rt && row < r_end;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                uint32_t w[U + 1];
+                if (rok && uok[g]) {
+                    const uint32_t *wb = a.bits + row * wpr + woff[g];
+                    w[0] = ju[g] ? wb[-1] : a.s0[row * a.bpr + ublk[g]];
+#pragma unroll
+                    for (int j = 0; j < U; ++j) w[j + 1] = wb[j];
+                } else {
+                    // no stream: state 0, multiplied by x = 0 or never summed into a row
+#pragma unroll
+                    for (int j = 0; j <= U; ++j) w[j] = 0u;
                 }
 #pragma unroll
-                for (int t = 0; t < R; ++t) {  // R tiles on
-                    c += step_c;
-                    ju += step_j;
-                    if (ju >= upb) {
-                        ju -= upb;
-                        ++c;
+                for (int j = 0; j < U; ++j) {
+                    wr[i][g][2 * j] = __builtin_amdgcn_alignbit(w[j], w[j + 1], 16);
+                    wr[i][g][2 * j + 1] = w[j + 1];
+                }
+            }
+        }
+        __syncthreads();  // the previous tile is done with the table and the row sums
+        col_copy_part<V>(tab, vec, a.C, 0, nfl, n4, tid);
+        __syncthreads();
+        for (int p = 0; p < a.parts; ++p) {
+            uint32_t negbase = 0u - static_cast<uint32_t>(p) * dummy;  // - part start
+            asm volatile("" : "+s"(negbase));  // kept as an addend: one v_lshl_add per step
+            // the states are extracted again in every pass (one instruction each) rather
+            // than kept in registers across passes
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int j = 0; j < NR; ++j) asm volatile("" : "+v"(wr[i][g][j]));
+#pragma unroll
+            for (int i = 0; i < RT; ++i) {
+                if (i < a.rt) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        // B gathers are issued before their products are added
+#pragma unroll
+                        for (int q0 = 0; q0 < S; q0 += Sh::B) {
+                            constexpr int B = Sh::B;
+                            float c[B][V];
+#pragma unroll
+                            for (int b = 0; b < B; ++b) {
+                                const int q = q0 + b;
+                                const int e = (q + 1) * KV;  // window end, bits into the unit
+                                const int j = (e - 1) >> 5;  // word w_{j+1} holds bit e - 1
+                                // the window [e - L, e) lies in w_{j+1} when it ends past the
+                                // word's first 16 bits, else in m_j
+                                const bool in_w = e - 32 * j > 16;
+                                const uint32_t src = in_w ? wr[i][g][2 * j + 1] : wr[i][g][2 * j];
+                                const uint32_t sh = in_w ? 32 * (j + 1) - e : 32 * j + 16 - e;
+                                const uint32_t st = __builtin_amdgcn_ubfe(src, sh, a.L);
+                                uint32_t off = (st << kLog) + negbase;  // wraps below the part
+                                off = off < dummy ? off : dummy;
+                                load_row<V>(c[b], reinterpret_cast<const char *>(tab) + off);
+                            }
+#pragma unroll
+                            for (int b = 0; b < B; ++b)
+#pragma unroll
+                                for (int v = 0; v < V; ++v)
+                                    acc[i] = __builtin_fmaf(c[b][v], xr[g][q0 + b][v], acc[i]);
+                        }
                     }
                 }
             }
-            for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-            if constexpr (R == 1) {
-                if (row < a.M && lane == 0) a.y[row] = (p == 0) ? acc : a.y[row] + acc;
-            } else {
-                // the R wave sums of the row, added in order
-                __shared__ float rpart[kGemvWaves];
-                if (lane == 0) rpart[wv] = acc;
+            if (p + 1 < a.parts) {
+                __syncthreads();  // every wave is done with part p
+                col_copy_part<V>(tab, vec, a.C, p + 1, nfl, n4, tid);
                 __syncthreads();
-                if (rsub == 0 && row < a.M && lane == 0) {
-                    float t = rpart[wv];
-                    for (int q = 1; q < R; ++q) t += rpart[wv + q];
-                    a.y[row] = (p == 0) ? t : a.y[row] + t;
-                }
-                __syncthreads();  // rpart is written again next iteration
+            }
+        }
+        // row sums: a 6-level DPP reduction in each wave, then the row group's waves in order
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            if (i < a.rt) {
+                const float t = wave_sum(acc[i]);
+                if (lane == 0) red[i][wv] = t;
+            }
+        }
+        __syncthreads();
+        const int cw = a.nt >> 6;  // waves per row group
+        if (active_rg && tc < a.rt) {
+            const int i = tc;
+            const int64_t row = t0 + rg + static_cast<int64_t>(a.rgroups) * i;
+            if (row < r_end) {
+                const int w0 = rg * cw;
+                float t = red[i][w0];
+                for (int w = 1; w < cw; ++w) t += red[i][w0 + w];
+                a.y[row] = t;
             }
         }
     }
 }
 
-// Any shape: lane l owns words l, l + 64, ... of the row and decodes every step whose
-// chunk ends inside its word (a chunk may straddle two words); x is read from global
-// memory.  Codebook parts in LDS as above.
+// Any shape: one wave per row; lane l owns words l, l + 64, ... of the row and decodes
+// every step whose chunk ends inside its word (a chunk may straddle two words); x is read
+// from global memory.  Codebook parts in LDS as above.  Summation order of y[r]: per pass,
+// each lane's fp32 chain over its words and their steps and coordinates, the 64 chains in
+// a 6-level shuffle tree, and the pass sums added to y[r] in pass order.
 __global__ __launch_bounds__(kGemvThreads) void gemv_generic_kernel(GemvArgs a) {
     extern __shared__ float tab[];
     const int tid = threadIdx.x;
@@ -231,7 +404,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_generic_kernel(GemvArgs a) 
 // from several host threads at once.
 hipError_t allow_lds(const void *kern) {
     static std::mutex mu;
-    static const void *done[48] = {};  // every kernel of this file
+    static const void *done[64] = {};  // every kernel of this file
     std::lock_guard<std::mutex> lock(mu);
     for (const void *k : done)
         if (k == kern) return hipSuccess;
@@ -262,6 +435,80 @@ int cu_count() {
 hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_state,
                               const float *C, const float *x, float *y, int64_t M, int64_t N,
                               int L, int k, int V, int T, hipStream_t s) {
+    const int kv = k * V;
+    const int n = T / V;
+    const int nwords = (k * T + 31) / 32;
+    const int64_t bpr = N / T;
+    const int64_t wpr = bpr * nwords;
+    const int64_t cus = cu_count();
+    // Column kernel: every block a whole number of units, a row of at most 1024 units.
+    const int U = kv / gcd_c(kv, 32);
+    const bool whole = wpr > 0 && (nwords % U == 0) &&
+                       (static_cast<int64_t>(kv) * n == static_cast<int64_t>(nwords) * 32);
+    const int64_t upr = whole ? wpr / U : 0;
+    const int64_t nt = upr >= kColThreads ? kColThreads : ((upr + 63) / 64) * 64;
+    const int64_t G = nt > 0 ? (upr + nt - 1) / nt : 0;
+    // (a row group of NT threads; R_G = 1024 / NT of them share a workgroup)
+    if (whole && G == 1 && (V == 1 || V == 2 || V == 4)) {
+        ColArgs a{};
+        a.bits = bitstream;
+        a.s0 = start_state;
+        a.C = C;
+        a.x = x;
+        a.y = y;
+        a.M = M;
+        a.bpr = bpr;
+        a.nwords = nwords;
+        a.upb = nwords / U;
+        a.upr = upr;
+        a.L = L;
+        a.nt = static_cast<int>(nt);
+        a.rgroups = static_cast<int>(kColThreads / nt);
+        int plog = L;
+        while ((int64_t{1} << plog) * V * 4 > kGemvPartBytes) --plog;
+        a.part_log2 = plog;
+        a.parts = 1 << (L - plog);
+        a.c_aligned = ((reinterpret_cast<uintptr_t>(C) & 15) == 0 &&
+                       ((int64_t{1} << plog) * V) % 4 == 0) ? 1 : 0;
+        int64_t grid = (M + a.rgroups - 1) / a.rgroups;
+        if (grid > cus) grid = cus;
+        if (grid < 1) grid = 1;
+        a.rows_per_wg = (M + grid - 1) / grid;
+        grid = (M + a.rows_per_wg - 1) / a.rows_per_wg;
+        const int64_t per_rg = (a.rows_per_wg + a.rgroups - 1) / a.rgroups;
+        const void *kern = nullptr;
+        int rt_max = 0;
+#define TCQ_COL_CASE(KV_, V_, G_)                                                         \
+    if (kv == KV_ && V == V_ && G == G_) {                                                \
+        kern = reinterpret_cast<const void *>(gemv_cols_kernel<KV_, V_, G_>);             \
+        rt_max = ColShape<KV_, V_, G_>::RT;                                               \
+    }
+#define TCQ_COL_CASES(KV_, V_) TCQ_COL_CASE(KV_, V_, 1)
+        TCQ_COL_CASES(1, 1)
+        TCQ_COL_CASES(2, 1)
+        TCQ_COL_CASES(2, 2)
+        TCQ_COL_CASES(3, 1)
+        TCQ_COL_CASES(4, 1)
+        TCQ_COL_CASES(4, 2)
+        TCQ_COL_CASES(4, 4)
+        TCQ_COL_CASES(6, 1)
+        TCQ_COL_CASES(6, 2)
+        TCQ_COL_CASES(8, 1)
+        TCQ_COL_CASES(8, 2)
+        TCQ_COL_CASES(8, 4)
+#undef TCQ_COL_CASES
+#undef TCQ_COL_CASE
+        if (kern) {
+            a.rt = static_cast<int>(per_rg < rt_max ? per_rg : rt_max);
+            void *args[] = {&a};  // (the kernel's LDS is static)
+            hipError_t e = hipLaunchKernel(kern, dim3(static_cast<unsigned>(grid)),
+                                           dim3(kColThreads), args, 0, s);
+            if (e != hipSuccess) return e;
+            return hipGetLastError();
+        }
+    }
+
+    // Any other shape: the generic kernel (one wave per row, x from global memory).
     GemvArgs a{};
     a.bits = bitstream;
     a.s0 = start_state;
@@ -269,81 +516,31 @@ hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_s
     a.x = x;
     a.y = y;
     a.M = M;
-    a.bpr = N / T;
-    a.nwords = (k * T + 31) / 32;
-    a.wpr = a.bpr * a.nwords;
+    a.bpr = bpr;
+    a.nwords = nwords;
+    a.wpr = wpr;
     a.L = L;
-    a.kv = k * V;
+    a.kv = kv;
     a.V = V;
-    a.n = T / V;
+    a.n = n;
     a.T = T;
     a.step_c = 64 / a.nwords;
     a.step_j = 64 % a.nwords;
-    // Tiled kernel when every block is a whole number of units (U words, S steps) and x
-    // fits beside a table part.
-    const int U = a.kv / gcd_c(a.kv, 32);
-    const int64_t S = 32 * U / a.kv;
-    const bool whole = a.wpr > 0 && (a.nwords % U == 0) &&
-                       (static_cast<int64_t>(a.kv) * a.n == static_cast<int64_t>(a.nwords) * 32);
-    const int64_t tiles = (a.wpr / U + 63) / 64;
-    a.xt_len = whole ? tiles * 64 * S * V : 0;
-    const int64_t xt_bytes = a.xt_len * 4;
-    const bool tiled = whole && xt_bytes + kGemvMinPartBytes <= kGemvLdsBytes;
-    const int64_t budget = tiled ? kGemvLdsBytes - xt_bytes : kGemvPartBytes;
-    // states per part: the largest power of two whose V floats fit in the budget
     int plog = 0;
-    while (plog < L && (int64_t{2} << plog) * V * 4 <= budget &&
-           (int64_t{2} << plog) * V * 4 <= kGemvPartBytes)
-        ++plog;
+    while (plog < L && (int64_t{2} << plog) * V * 4 <= kGemvPartBytes) ++plog;
     a.part_log2 = plog;
     a.parts = 1 << (L - plog);
-    const int64_t cus = cu_count();
-    // tiled kernel with rows too few to give every CU a workgroup of one-row waves: R
-    // waves share a row (at most 4, and no more than a row has tiles of 64 units)
-    int rsplit = 1;
-    while (rsplit < 4 && (M * rsplit * 2 + kGemvWaves - 1) / kGemvWaves <= cus &&
-           rsplit * 2 <= tiles)
-        rsplit *= 2;
-    const void *kern = reinterpret_cast<const void *>(gemv_generic_kernel);
-    if (tiled && (V == 1 || V == 2 || V == 4)) {
-#define TCQ_GEMV_CASE(KV_, V_)                                                            \
-    if (a.kv == KV_ && V == V_)                                                          \
-        kern = rsplit == 4   ? reinterpret_cast<const void *>(gemv_tiled_kernel<KV_, V_, 4>) \
-               : rsplit == 2 ? reinterpret_cast<const void *>(gemv_tiled_kernel<KV_, V_, 2>) \
-                             : reinterpret_cast<const void *>(gemv_tiled_kernel<KV_, V_, 1>);
-        TCQ_GEMV_CASE(1, 1)
-        TCQ_GEMV_CASE(2, 1)
-        TCQ_GEMV_CASE(2, 2)
-        TCQ_GEMV_CASE(3, 1)
-        TCQ_GEMV_CASE(4, 1)
-        TCQ_GEMV_CASE(4, 2)
-        TCQ_GEMV_CASE(4, 4)
-        TCQ_GEMV_CASE(6, 2)
-        TCQ_GEMV_CASE(8, 1)
-        TCQ_GEMV_CASE(8, 2)
-        TCQ_GEMV_CASE(8, 4)
-#undef TCQ_GEMV_CASE
-    }
-    if (kern == reinterpret_cast<const void *>(gemv_generic_kernel)) {
-        // the generic kernel keeps x in global memory: give the table the whole budget
-        plog = 0;
-        while (plog < L && (int64_t{2} << plog) * V * 4 <= kGemvPartBytes) ++plog;
-        a.part_log2 = plog;
-        a.parts = 1 << (L - plog);
-    }
-    const bool use_xt = kern != reinterpret_cast<const void *>(gemv_generic_kernel);
-    if (!use_xt) rsplit = 1;  // the generic kernel has one wave per row
     int64_t grid = cus;
-    const int64_t need = (M * rsplit + kGemvWaves - 1) / kGemvWaves;
+    const int64_t need = (M + kGemvWaves - 1) / kGemvWaves;
     if (grid > need) grid = need;
     if (grid < 1) grid = 1;
-    const size_t shmem = (size_t{1} << plog) * V * sizeof(float) +
-                         (use_xt ? static_cast<size_t>(xt_bytes) : 0);
+    const size_t shmem = (size_t{1} << plog) * V * sizeof(float);
+    const void *kern = reinterpret_cast<const void *>(gemv_generic_kernel);
     hipError_t e = allow_lds(kern);
     if (e != hipSuccess) return e;
     void *args[] = {&a};
-    e = hipLaunchKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(kGemvThreads), args,
-                        shmem, s);
+    e = hipLaunchKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(kGemvThreads), args, shmem,
+                        s);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }
