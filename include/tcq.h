@@ -139,6 +139,26 @@ int tcq_encode_timed(const float *W, int64_t M, int64_t N, int64_t ldw, const fl
                      hipEvent_t acs_begin, hipEvent_t acs_end);
 
 /*
+ * tcq_encode_noalloc -- tcq_encode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, outputs and errors as tcq_encode, without the workspace: the library uses a
+ * file-scope device array of TCQ_NOALLOC_SCRATCH_BYTES (256 MiB) as the workspace, which
+ * every GPU it runs on holds from the first call on that GPU until the process ends.  The
+ * call allocates nothing (no hipMalloc, no hipFree); the device address of the array is
+ * looked up once per GPU.  Blocks are encoded in batches that fit the scratch (255 blocks
+ * at L = 16, k*V = 2, T = 256), so any number of rows is accepted; a shape whose single block
+ * needs more scratch than that is rejected with TCQ_EUNSUPPORTED (no shape within the GPU
+ * limits does: the largest, L = 16, k = 2, V = 2, T = 2048, needs 9.5 MiB).  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (two streams, two host threads) race and must be
+ * serialised by the caller.  Nothing in the array needs to start at zero.
+ */
+#define TCQ_NOALLOC_SCRATCH_BYTES (256ull << 20)
+int tcq_encode_noalloc(const float *W, int64_t M, int64_t N, int64_t ldw, const float *d,
+                       const float *codebook, int L, int k, int V, int T, uint32_t *bitstream,
+                       uint32_t *start_state, float *cost, float *recon, int64_t ldr,
+                       hipStream_t stream);
+
+/*
  * tcq_decode -- rebuild weights from bitstreams (Pingala-8 post: decoding reads bits,
  * updates the state and looks up values).
  *   bitstream, start_state : device, as written by tcq_encode for an M x N problem

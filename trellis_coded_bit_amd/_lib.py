@@ -23,7 +23,7 @@ TCQ_ENOMEM = -5
 
 EXPORTED = ("tcq_version", "tcq_last_error", "tcq_make_codebook",
             "tcq_encode_workspace_bytes", "tcq_encode_workspace_min_bytes", "tcq_encode",
-            "tcq_encode_timed", "tcq_decode", "tcq_decode_gemv",
+            "tcq_encode_timed", "tcq_encode_noalloc", "tcq_decode", "tcq_decode_gemv",
             "tcq_ldlq_workspace_bytes", "tcq_encode_ldlq", "tcq_bcjr_workspace_bytes",
             "tcq_bcjr", "tcq_hadamard", "tcq_scale_field_workspace_bytes", "tcq_scale_field")
 
@@ -62,6 +62,9 @@ def load():
     lib.tcq_encode_timed.restype = i32
     lib.tcq_encode_timed.argtypes = [vp, i64, i64, i64, vp, vp, i32, i32, i32, i32, vp, vp, vp,
                                      vp, i64, vp, sz, vp, vp, vp]
+    lib.tcq_encode_noalloc.restype = i32
+    lib.tcq_encode_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, i32, i32, i32, i32, vp, vp,
+                                       vp, vp, i64, vp]
     lib.tcq_decode.restype = i32
     lib.tcq_decode.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, i64, vp]
     lib.tcq_decode_gemv.restype = i32
@@ -141,6 +144,14 @@ def tcq_encode_timed(W: int, M: int, N: int, ldw: int, d: int | None, codebook: 
                                    start_state, cost, recon or None, ldr, workspace,
                                    workspace_bytes, stream or None, acs_begin or None,
                                    acs_end or None))
+
+
+def tcq_encode_noalloc(W: int, M: int, N: int, ldw: int, d: int | None, codebook: int,
+                       L: int, k: int, V: int, T: int, bitstream: int, start_state: int,
+                       cost: int, recon: int | None, ldr: int, stream: int | None) -> None:
+    _check("tcq_encode_noalloc",
+           load().tcq_encode_noalloc(W, M, N, ldw, d or None, codebook, L, k, V, T, bitstream,
+                                     start_state, cost, recon or None, ldr, stream or None))
 
 
 def tcq_decode(bitstream: int, start_state: int, codebook: int, M: int, N: int, L: int,

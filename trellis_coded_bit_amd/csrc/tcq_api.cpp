@@ -169,11 +169,11 @@ extern "C" int tcq_encode_workspace_bytes(int64_t M, int64_t N, int L, int k, in
     return TCQ_OK;
 }
 
-static int encode_impl(const char *fn, const float *W, int64_t M, int64_t N, int64_t ldw,
-                       const float *d, const float *codebook, int L, int k, int V, int T,
-                       uint32_t *bitstream, uint32_t *start_state, float *cost, float *recon,
-                       int64_t ldr, void *workspace, size_t workspace_bytes,
-                       hipStream_t stream, hipEvent_t acs_begin, hipEvent_t acs_end) {
+int tcq::encode_impl(const char *fn, const float *W, int64_t M, int64_t N, int64_t ldw,
+                     const float *d, const float *codebook, int L, int k, int V, int T,
+                     uint32_t *bitstream, uint32_t *start_state, float *cost, float *recon,
+                     int64_t ldr, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                     hipEvent_t acs_begin, hipEvent_t acs_end) {
     clear_error();
     int rc = check_trellis(fn, M, N, L, k, V, T);
     if (rc != TCQ_OK) return rc;

@@ -40,6 +40,18 @@ enum Variant : int {
 
 Plan plan_for(const Problem &p);
 
+// The encoder behind tcq_encode / tcq_encode_timed (tcq_api.cpp): checks the arguments,
+// plans the batches for the given workspace and enqueues every kernel.  `fn` names the
+// entry point in error messages.  It allocates nothing.
+int encode_impl(const char *fn, const float *W, int64_t M, int64_t N, int64_t ldw,
+                const float *d, const float *codebook, int L, int k, int V, int T,
+                uint32_t *bitstream, uint32_t *start_state, float *cost, float *recon,
+                int64_t ldr, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                hipEvent_t acs_begin, hipEvent_t acs_end);
+
+// Per-thread error message of the C ABI (tcq_last_error).
+void set_error(const char *fmt, ...);
+
 // Kernel launchers (return hipError_t of the launch).
 hipError_t launch_acs_generic(const Problem &p, const Plan &pl, const float *W,
                               const float *d, const float *C, int64_t block0, int64_t nb,
