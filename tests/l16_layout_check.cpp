@@ -10,7 +10,9 @@
 //    writing and the reading side, and every wave instruction touches distinct banks
 //    (64 banks per wave, 32 per half wave);
 //  - the k*V = 4 half-step patterns place the metric on the even half-steps and list
-//    every metric group once, in processing order.
+//    every metric group once, in processing order;
+//  - the k*V = 4 relabelling of the state commutes with the shift and makes the two
+//    half-step minima pick the lowest predecessor index.
 #define __host__
 #define __device__
 #include <cstdio>
@@ -218,6 +220,52 @@ int main() {
                 CHECK(seg_has_metric(q & 1, seg) == ((3 * q + seg_step(seg)) % 2 == 0));
         // ring sizes 8 V divide the positions of every super-step
         for (int V = 1; V <= 2; ++V) CHECK((metric_groups(mp) * V) % (8 * V) == 0);
+    }
+    // k*V = 4 relabelling P (halves of every nibble exchanged): an involution that
+    // commutes with the 4-bit shift, so the relabelled trellis has the same paths; its
+    // first half-step drops j_lo (bits 13:12 of the true state), the second j_hi.
+    for (uint32_t s = 0; s < (1u << 16); ++s) {
+        CHECK(nibble_halves_swap(nibble_halves_swap(s)) == s);
+        CHECK((nibble_halves_swap(s) >> 14) == ((s >> 12) & 3u));
+        CHECK(((nibble_halves_swap(s) >> 12) & 3u) == (s >> 14));
+        for (uint32_t b = 0; b < 16; ++b)
+            CHECK(nibble_halves_swap(((s << 4) | b) & 0xFFFFu) ==
+                  (((nibble_halves_swap(s) << 4) | nibble_halves_swap(b)) & 0xFFFFu));
+    }
+    // Two-stage minimum over j = 4 j_hi + j_lo: first, per j_hi, the lowest j_lo of
+    // minimum cost; then the lowest j_hi of minimum cost.  It picks the lowest j of
+    // minimum cost, for every cost vector with values in {0, 1, 2} on a 16-way group
+    // (sampled: the 2^16 vectors over {0, 1} and 3^8 patterns spread over the group).
+    auto check_two_stage = [&](const int (&c)[16]) {
+        int best = 0;
+        for (int j = 1; j < 16; ++j)
+            if (c[j] < c[best]) best = j;
+        int m1[4], a1[4];
+        for (int hi = 0; hi < 4; ++hi) {
+            a1[hi] = 0;
+            for (int lo = 1; lo < 4; ++lo)
+                if (c[4 * hi + lo] < c[4 * hi + a1[hi]]) a1[hi] = lo;
+            m1[hi] = c[4 * hi + a1[hi]];
+        }
+        int hi_best = 0;
+        for (int hi = 1; hi < 4; ++hi)
+            if (m1[hi] < m1[hi_best]) hi_best = hi;
+        CHECK(4 * hi_best + a1[hi_best] == best);
+    };
+    for (uint32_t m = 0; m < (1u << 16); ++m) {
+        int c[16];
+        for (int j = 0; j < 16; ++j) c[j] = (m >> j) & 1u;
+        check_two_stage(c);
+    }
+    for (uint32_t m = 0; m < 6561; ++m) {
+        int c[16];
+        uint32_t t = m;
+        for (int j = 0; j < 8; ++j) {
+            c[2 * j] = t % 3;
+            c[2 * j + 1] = (t % 3 + j) % 3;
+            t /= 3;
+        }
+        check_two_stage(c);
     }
     if (fails) {
         std::printf("%d failures\n", fails);

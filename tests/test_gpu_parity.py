@@ -167,22 +167,20 @@ def test_strided_rows_and_empty(oracle_lib):
 
 
 # Exact ties everywhere: weights on a 1/4 grid and a codebook rounded to halves make every
-# cost exact in fp32, so many paths tie.  The kernels that take the minimum over all
-# predecessors of a group at once (generic, L=16 with k*V = 2 or 3) must reproduce the
-# oracle's lowest-index choice bit for bit.  The k*V = 4 kernel takes its minimum in two
-# 2-bit halves; on an exact tie it may keep a different path of the same cost (lowest
-# bottom pair first), so there the unique results are compared (the cost, bitwise) and
-# the path it kept is checked to be a valid optimal path.
+# cost exact in fp32, so many paths tie.  Every kernel family (generic; L=16 with k*V = 2,
+# 3, and 4, the last in half-steps on the relabelled state) must reproduce the oracle's
+# lowest-index choice bit for bit.
 TIE_CASES = [
     # L, k, V, T, M, N, split_min
     (8, 2, 1, 32, 4, 128, False),
     (12, 3, 1, 30, 3, 90, False),
     (16, 2, 1, 64, 3, 192, False),
     (16, 3, 1, 64, 2, 128, False),
-    (16, 2, 2, 64, 3, 192, True),
-    (16, 4, 1, 32, 2, 64, True),
+    (16, 2, 2, 64, 3, 192, False),
+    (16, 4, 1, 32, 2, 64, False),
+    (16, 2, 2, 256, 4, 1024, False),
+    (16, 4, 1, 256, 2, 512, False),
 ]
-
 
 @pytest.mark.parametrize("L,k,V,T,M,N,split_min", TIE_CASES)
 @pytest.mark.parametrize("weighted", [False, True])

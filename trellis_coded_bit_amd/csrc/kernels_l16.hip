@@ -324,7 +324,10 @@ __device__ __forceinline__ uint32_t bp_choice(const uint2 *bpb, int t, uint32_t 
 // One wave per block: follow the remembered predecessors back from the end state and
 // pack the 2-bit chunks b_1..b_n, MSB first, into MSB-first words.  n counts 2-bit
 // steps: the half-step view of k*V = 4 has twice the steps of the block, up to
-// 2 * TCQ_MAX_STEPS.  Three steps per memory round trip: with s_t known, lane 0 reads
+// 2 * TCQ_MAX_STEPS.  With swap_halves (the relabelled trellis of the k*V = 4 kernel,
+// whose state has the two halves of every nibble exchanged) the end state is given as a
+// true state and converted first, and the start state and every packed word are
+// converted back at the end.  Three steps per memory round trip: with s_t known, lane 0 reads
 // the choice at step t for s_t, lanes 1..4 the choice at step t-1 for each of the four
 // possible s_{t-1}, and lanes 5..20 the choice at step t-2 for each of the sixteen
 // possible s_{t-2}; the three reads are independent, and the wave then picks the path
@@ -333,12 +336,13 @@ __device__ __forceinline__ uint32_t bp_choice(const uint2 *bpb, int t, uint32_t 
 __global__ __launch_bounds__(64) void traceback_l16_kernel(
     const uint2 *__restrict__ bp, int64_t bp_per_block, const uint32_t *__restrict__ send,
     int n, int nwords, int64_t block0, uint32_t *__restrict__ bitstream,
-    uint32_t *__restrict__ start_state) {
+    uint32_t *__restrict__ start_state, int swap_halves) {
     __shared__ uint8_t chunk[2 * TCQ_MAX_STEPS];
     const int lane = threadIdx.x;
     const uint2 *bpb = bp + blockIdx.x * bp_per_block;
     const int64_t blk = block0 + blockIdx.x;
     uint32_t s = send[blockIdx.x];  // s_t, the same in every lane
+    if (swap_halves) s = nibble_halves_swap(s);
     int t = n;
     while (t >= 1) {
         // this lane's candidate: level 0 is s_t itself, level 1 s_{t-1} = (j0 << 14) |
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(64) void traceback_l16_kernel(
         s = (j2 << 14) | (s2 >> 2);
         t -= 3;
     }
-    if (lane == 0) start_state[blk] = s;
+    if (lane == 0) start_state[blk] = swap_halves ? nibble_halves_swap(s) : s;
     __syncthreads();
     for (int wi = lane; wi < nwords; wi += 64) {
         uint32_t word = 0;
@@ -387,7 +391,7 @@ __global__ __launch_bounds__(64) void traceback_l16_kernel(
             const int ci = wi * 16 + q;
             if (ci < n) word |= static_cast<uint32_t>(chunk[ci]) << (30 - 2 * q);
         }
-        bitstream[blk * nwords + wi] = word;
+        bitstream[blk * nwords + wi] = swap_halves ? nibble_halves_swap(word) : word;
     }
 }
 
@@ -441,14 +445,14 @@ hipError_t launch_acs_l16(const Problem &p, const Plan &pl, const float *W, cons
 
 hipError_t launch_traceback_l16(const Problem &p, const Plan &pl, int64_t block0, int64_t nb,
                                 const char *ws, uint32_t *bitstream, uint32_t *start_state,
-                                hipStream_t s) {
+                                hipStream_t s, bool swap_halves) {
     const char *per = ws + pl.fixed;
     const uint2 *bp = reinterpret_cast<const uint2 *>(per);
     const uint32_t *send = reinterpret_cast<const uint32_t *>(per + nb * pl.bp_bytes);
     const int nwords = (p.k * p.T + 31) / 32;
     hipLaunchKernelGGL(traceback_l16_kernel, dim3(static_cast<unsigned>(nb)), dim3(64), 0, s, bp,
                        static_cast<int64_t>(pl.bp_bytes / sizeof(uint2)), send, p.n, nwords,
-                       block0, bitstream, start_state);
+                       block0, bitstream, start_state, swap_halves ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -1,15 +1,20 @@
 // L = 16, k*V = 4 forward kernel (k = 2, V = 2: the 8B-MLP shape; also k = 4, V = 1).
 //
-// A step that shifts in four bits is two "half-steps" of two bits: the predecessors of
-// s = (x << 4) | b are (j << 12) | x, j = 0..15, and the minimum over j splits into a
-// minimum over the top two bits of j (first half-step, which adds no cost) followed by a
-// minimum over the bottom two (second half-step, which adds the branch metric of the
-// whole step).  The minima are exact, so every cost is the one the 16-way search gives;
-// the bitstream is the same bits read as 2-bit chunks (chunk b_t = (b'_{2t-1} << 2) |
-// b'_{2t}), and the start state s_0 comes out below 2^12 because all costs start equal.
-// Only exact ties between predecessors can be resolved differently from the 16-way
-// search (lowest bottom pair first instead of lowest j), and an exact tie is a runner-up
-// at zero distance.
+// A step that shifts in four bits is two "half-steps" of two bits.  The predecessors of
+// s = (x << 4) | b are (j << 12) | x, j = 0..15; write j = 4 j_hi + j_lo.  The kernel runs
+// the trellis on a relabelled state: each 4-bit chunk of the state is stored with its two
+// 2-bit halves exchanged, P(s) (P swaps bits [3:2] and [1:0] of every nibble; P = P^-1).
+// A 4-bit shift of s is a 4-bit shift of P(s), so every path and cost is unchanged; but
+// the first half-step of a step now drops the oldest 2-bit digit of P(s), which is j_lo,
+// and the second drops j_hi.  The first half-step (no cost added) keeps, for every j_hi,
+// the lowest j_lo of minimum cost; the second (which adds the branch metric of the whole
+// step on the true state, C[P(.)]) keeps the lowest j_hi of minimum cost.  Together they
+// keep the smallest j = 4 j_hi + j_lo of minimum cost: the 16-way lowest-index rule.  The
+// minima are exact, so every cost is the one the 16-way search gives.  The half-step
+// chunks come out as (low half, high half) of each true chunk, so the traceback swaps the
+// halves of every nibble of the packed stream and of the start state; the end state is
+// chosen by the lowest true index.  The start state comes out below 2^12 because all
+// costs start equal.
 //
 // So the kernel is the k*V = 2 kernel (kernels_l16.hip, layout in l16_layout.h) run over
 // 2n half-steps, with the metric only on even half-steps: half-step h = 3q + P of
@@ -49,9 +54,12 @@ __global__ __launch_bounds__(256) void l16h_prepare_kernel(const float *__restri
     const uint32_t w = rem / (kGroupsPerLane * kLanes);
     const uint32_t g = (rem / kLanes) % kGroupsPerLane;
     const uint32_t l = rem % kLanes;
-    const uint32_t s = state_of(p, w, l, group_reg(p, g, 0));  // successors s .. s+3
-    const float *src = C + static_cast<size_t>(s) * V + v;
-    out[idx] = make_float4(src[0], src[V], src[2 * V], src[3 * V]);
+    // successors s .. s + 3 of the relabelled trellis: true states P(s + b)
+    const uint32_t s = state_of(p, w, l, group_reg(p, g, 0));
+    out[idx] = make_float4(C[static_cast<size_t>(nibble_halves_swap(s)) * V + v],
+                           C[static_cast<size_t>(nibble_halves_swap(s + 1)) * V + v],
+                           C[static_cast<size_t>(nibble_halves_swap(s + 2)) * V + v],
+                           C[static_cast<size_t>(nibble_halves_swap(s + 3)) * V + v]);
 }
 
 template <int V>
@@ -292,10 +300,11 @@ __device__ __forceinline__ void tail_h(uint32_t (&J)[kRegs], float4 (&ring)[Ring
 template <int P, int NM>
 __device__ __forceinline__ void lane_argmin_h(const uint32_t (&J)[kRegs], uint32_t w,
                                               uint32_t l, uint32_t &bv, uint32_t &bi) {
-    const uint32_t lanepart = state_of(P, w, l, 0);
+    // ties between end states go to the lowest true index P(state)
+    const uint32_t lanepart = nibble_halves_swap(state_of(P, w, l, 0));
 #pragma unroll
     for (int r = 0; r < kRegs; ++r) {
-        const uint32_t s = lanepart | state_of(P, 0, 0, r);
+        const uint32_t s = lanepart | nibble_halves_swap(state_of(P, 0, 0, r));
         const uint32_t v = J[phys(NM, r)];
         if (v < bv || (v == bv && s < bi)) {
             bv = v;

@@ -166,6 +166,15 @@ __host__ __device__ constexpr uint32_t bp_shift(int p, uint32_t g) {
 }
 
 // ---------------------------------------------------------------------------------
+// k*V = 4 run as 2-bit half-steps (kernels_l16h.hip) on a relabelled state: bits [3:2]
+// and [1:0] of every nibble exchanged.  The map is a permutation of bit positions, so
+// it is its own inverse and the image of an OR is the OR of the images.
+// ---------------------------------------------------------------------------------
+__host__ __device__ constexpr uint32_t nibble_halves_swap(uint32_t x) {
+    return ((x & 0x33333333u) << 2) | ((x >> 2) & 0x33333333u);
+}
+
+// ---------------------------------------------------------------------------------
 // k*V = 4 run as 2-bit half-steps (kernels_l16h.hip): super-step q covers half-steps
 // 3q + 1 .. 3q + 3 and the metric sits on the even ones, i.e. on step P of the
 // super-step when q + P is even.  MP = q mod 2 is the super-step's pattern.

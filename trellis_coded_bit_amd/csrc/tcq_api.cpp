@@ -238,14 +238,15 @@ int tcq::encode_impl(const char *fn, const float *W, int64_t M, int64_t N, int64
                 e = hipEventRecord(acs_end, stream);
                 if (e != hipSuccess) return hip_fail(fn, "hipEventRecord", e);
             }
-            // the 2-bit half-step view: 2n steps of k = 2, V = 1 give the same bits
+            // the 2-bit half-step view: 2n steps of k = 2, V = 1 on the relabelled state
+            // (halves of every nibble exchanged), converted back by the traceback
             Problem ph = p;
             ph.k = 2;
             ph.V = 1;
             ph.kv = 2;
             ph.n = 2 * p.n;
             ph.T = 2 * p.n;
-            e = launch_traceback_l16(ph, pl, b0, nb, ws, bitstream, start_state, stream);
+            e = launch_traceback_l16(ph, pl, b0, nb, ws, bitstream, start_state, stream, true);
             if (e != hipSuccess) return hip_fail(fn, "traceback launch", e);
         } else if (pl.variant == kL16RegsK3) {
             e = launch_acs_l16k3(p, pl, W, d, b0, nb, ws, cost, stream);

@@ -105,9 +105,10 @@ size_t l16_bp_bytes(const Problem &p);
 hipError_t launch_l16_prepare(const Problem &p, const float *C, char *fixed_ws, hipStream_t s);
 hipError_t launch_acs_l16(const Problem &p, const Plan &pl, const float *W, const float *d,
                           int64_t block0, int64_t nb, char *ws, float *cost, hipStream_t s);
+// swap_halves: the k*V = 4 kernel's relabelled trellis (kernels_l16h.hip)
 hipError_t launch_traceback_l16(const Problem &p, const Plan &pl, int64_t block0, int64_t nb,
                                 const char *ws, uint32_t *bitstream, uint32_t *start_state,
-                                hipStream_t s);
+                                hipStream_t s, bool swap_halves = false);
 
 // L = 16, k*V = 4 register-resident path (half-steps).
 bool l16h_supported(const Problem &p);
