@@ -66,7 +66,7 @@ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 // added in wave order.
 constexpr int kColThreads = 1024;
 constexpr int kColWaves = kColThreads / 64;
-constexpr int kColRowsMax = 12;   // rows of a tile, per thread, at most
+constexpr int kColRowsMax = 14;   // rows of a tile, per thread, at most
 constexpr int kColRegBudget = 66;  // registers for x, a tile's stream words and sums
 constexpr int kColBatch = 8;       // table gathers in flight per thread
 constexpr int kColTabFloats = static_cast<int>(kGemvPartBytes / 4);  // largest part
@@ -106,8 +106,10 @@ struct ColShape {
     static constexpr int kLeft =
         kBudget - G * S * V - (G * S * V >= 32 && V > 1 ? 16 : 0) - B * V;
     static constexpr int kFit = kLeft / (G * NR + 1);
-    // (three-word units keep 32 x values and six stream registers per row: fewer rows)
-    static constexpr int kCap = U == 1 ? kColRowsMax : kColRowsMax / 2;
+    // (caps measured on MI355X: two-float rows run 14 rows at a time -- 14336 x 4096 in
+    // one tile per workgroup -- while one- and four-float rows gain nothing past 12 and
+    // spill above it; three-word units keep 32 x values and six stream registers per row)
+    static constexpr int kCap = U == 1 ? (V == 2 ? 14 : 12) : 6;
     static constexpr int RT = kFit < 1 ? 1 : (kFit > kCap ? kCap : kFit);
 };
 
@@ -237,6 +239,11 @@ __global__ __launch_bounds__(kColThreads) void gemv_cols_kernel(ColArgs a) {
     if (r_end > a.M) r_end = a.M;
     const int64_t tile_rows = static_cast<int64_t>(a.rgroups) * a.rt;
     for (int64_t t0 = r_begin; t0 < r_end; t0 += tile_rows) {
+        // rows of this row group in the tile (uniform per wave): the rest are skipped
+        int64_t here = 0;
+        if (active_rg && t0 + rg < r_end)
+            here = (r_end - t0 - rg + a.rgroups - 1) / a.rgroups;
+        const int nrows = static_cast<int>(here < a.rt ? here : a.rt);
         // stream registers of the tile
         uint32_t wr[RT][G][NR];
         float acc[RT];
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(kColThreads) void gemv_cols_kernel(ColArgs a) {
         for (int i = 0; i < RT; ++i) {
             acc[i] = 0.0f;
             const int64_t row = t0 + rg + static_cast<int64_t>(a.rgroups) * i;
-            const bool rok = active_rg && i < a.rt && row < r_end;
+            const bool rok = i < nrows;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 uint32_t w[U + 1];
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(kColThreads) void gemv_cols_kernel(ColArgs a) {
                     for (int j = 0; j < NR; ++j) asm volatile("" : "+v"(wr[i][g][j]));
 #pragma unroll
             for (int i = 0; i < RT; ++i) {
-                if (i < a.rt) {
+                if (i < nrows) {
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
                         // B gathers are issued before their products are added
@@ -322,17 +329,17 @@ __global__ __launch_bounds__(kColThreads) void gemv_cols_kernel(ColArgs a) {
         // row sums: a 6-level DPP reduction in each wave, then the row group's waves in order
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
-            if (i < a.rt) {
+            if (i < nrows) {
                 const float t = wave_sum(acc[i]);
                 if (lane == 0) red[i][wv] = t;
             }
         }
         __syncthreads();
         const int cw = a.nt >> 6;  // waves per row group
-        if (active_rg && tc < a.rt) {
+        if (tc < nrows) {
             const int i = tc;
             const int64_t row = t0 + rg + static_cast<int64_t>(a.rgroups) * i;
-            if (row < r_end) {
+            {
                 const int w0 = rg * cw;
                 float t = red[i][w0];
                 for (int w = 1; w < cw; ++w) t += red[i][w0 + w];
@@ -499,7 +506,9 @@ hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_s
 #undef TCQ_COL_CASES
 #undef TCQ_COL_CASE
         if (kern) {
-            a.rt = static_cast<int>(per_rg < rt_max ? per_rg : rt_max);
+            // the fewest tiles per row group, then rows spread evenly over them
+            const int64_t tiles = (per_rg + rt_max - 1) / rt_max;
+            a.rt = static_cast<int>((per_rg + tiles - 1) / tiles);
             void *args[] = {&a};  // (the kernel's LDS is static)
             hipError_t e = hipLaunchKernel(kern, dim3(static_cast<unsigned>(grid)),
                                            dim3(kColThreads), args, 0, s);
