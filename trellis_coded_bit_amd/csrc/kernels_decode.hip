@@ -1,6 +1,6 @@
-// y = W_hat x with the weights decoded inside the product (Pingala-8 post, decoding
-// paragraph: decoding reads bits, updates the state and looks values up, inside the
-// matrix-vector product).
+// Decoding (Pingala-8 post, decoding paragraph: decoding reads bits, updates the state and
+// looks values up, also inside the matrix-vector product): W_hat itself (tcq_decode) and
+// y = W_hat x with the weights decoded inside the product (tcq_decode_gemv).
 //
 // The state of step t is the L-bit window of s_0 || b_1 || ... || b_n that ends with
 // chunk b_t, so it can be read straight from two neighbouring 32-bit words of the stream
@@ -8,9 +8,9 @@
 //
 // The codebook (2^L x V floats; 256 KiB at L=16, V=1) is read at random, one entry per
 // step.  From L2 every such read pulls a whole cache line into L1, so the table is staged
-// through LDS instead, 128 KiB at a time: P = table / part passes, each adding the
-// products whose state falls in the part held in LDS.  Results are deterministic: every
-// row is summed in a fixed order (stated with each kernel).
+// through LDS instead, 128 KiB at a time: P = table / part passes, each taking the steps
+// whose state falls in the part held in LDS.  Results are deterministic: every row is
+// summed in a fixed order (stated with each kernel), and decoded values are copies.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -139,7 +139,7 @@ constexpr int log2_row_bytes() { return V == 1 ? 2 : (V == 2 ? 3 : 4); }
 // Part p of the table into LDS, then the row of zeros after it.  With 16-byte aligned
 // parts of at most 8 x 1024 float4, each thread issues its eight loads (the index clamped,
 // so every load is in bounds) before storing them.
-template <int V>
+template <int V, int THREADS = kColThreads>
 __device__ __forceinline__ void col_copy_part(float *tab, bool vec, const float *C, int p,
                                               int64_t nfl, int64_t n4, int tid) {
     if (vec) {
@@ -148,17 +148,17 @@ __device__ __forceinline__ void col_copy_part(float *tab, bool vec, const float 
         float4 t[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int64_t j = static_cast<int64_t>(u) * kColThreads + tid;
+            const int64_t j = static_cast<int64_t>(u) * THREADS + tid;
             t[u] = s4[j < n4 ? j : n4 - 1];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int64_t j = static_cast<int64_t>(u) * kColThreads + tid;
+            const int64_t j = static_cast<int64_t>(u) * THREADS + tid;
             if (j < n4) d4[j] = t[u];
         }
     } else {
         const float *src = C + static_cast<int64_t>(p) * nfl;
-        for (int64_t j = tid; j < nfl; j += kColThreads) tab[j] = src[j];
+        for (int64_t j = tid; j < nfl; j += THREADS) tab[j] = src[j];
     }
     if (tid < 4) tab[nfl + tid] = 0.0f;
 }
@@ -179,6 +179,33 @@ __device__ __forceinline__ void load_row(float (&c)[V], const char *p) {
         c[2] = t.z;
         c[3] = t.w;
     }
+}
+
+// Stream registers of one unit: from the word before it (w_0: the previous word of the
+// block, or s_0 for a block's first unit) and its U words, the words w_j and the words
+// m_j = w_j[15:0] w_{j+1}[31:16] that straddle them, as m_0, w_1, m_1, w_2, ..., w_U.  Every
+// L-bit state window (L <= 16) of the unit then lies inside one of these registers.
+template <int U>
+__device__ __forceinline__ void unit_regs(uint32_t (&wr)[2 * U], const uint32_t (&w)[U + 1]) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        wr[2 * j] = __builtin_amdgcn_alignbit(w[j], w[j + 1], 16);
+        wr[2 * j + 1] = w[j + 1];
+    }
+}
+
+// State of step q (0-based; a constant once the caller's loop is unrolled) of a unit: one
+// bit-field extract from the register that holds its window.
+template <int KV, int NR>
+__device__ __forceinline__ uint32_t unit_state(const uint32_t (&wr)[NR], int q, int L) {
+    const int e = (q + 1) * KV;  // window end, bits into the unit
+    const int j = (e - 1) >> 5;  // word w_{j+1} holds bit e - 1
+    // the window [e - L, e) lies in w_{j+1} when it ends past the word's first 16 bits,
+    // else in m_j
+    const bool in_w = e - 32 * j > 16;
+    const uint32_t src = in_w ? wr[2 * j + 1] : wr[2 * j];
+    const uint32_t sh = in_w ? 32 * (j + 1) - e : 32 * j + 16 - e;
+    return __builtin_amdgcn_ubfe(src, sh, L);
 }
 
 template <int KV, int V, int G>
@@ -265,11 +292,7 @@ __global__ __launch_bounds__(kColThreads) void gemv_cols_kernel(ColArgs a) {
 #pragma unroll
                     for (int j = 0; j <= U; ++j) w[j] = 0u;
                 }
-#pragma unroll
-                for (int j = 0; j < U; ++j) {
-                    wr[i][g][2 * j] = __builtin_amdgcn_alignbit(w[j], w[j + 1], 16);
-                    wr[i][g][2 * j + 1] = w[j + 1];
-                }
+                unit_regs<U>(wr[i][g], w);
             }
         }
         __syncthreads();  // the previous tile is done with the table and the row sums
@@ -298,15 +321,7 @@ __global__ __launch_bounds__(kColThreads) void gemv_cols_kernel(ColArgs a) {
                             float c[B][V];
 #pragma unroll
                             for (int b = 0; b < B; ++b) {
-                                const int q = q0 + b;
-                                const int e = (q + 1) * KV;  // window end, bits into the unit
-                                const int j = (e - 1) >> 5;  // word w_{j+1} holds bit e - 1
-                                // the window [e - L, e) lies in w_{j+1} when it ends past the
-                                // word's first 16 bits, else in m_j
-                                const bool in_w = e - 32 * j > 16;
-                                const uint32_t src = in_w ? wr[i][g][2 * j + 1] : wr[i][g][2 * j];
-                                const uint32_t sh = in_w ? 32 * (j + 1) - e : 32 * j + 16 - e;
-                                const uint32_t st = __builtin_amdgcn_ubfe(src, sh, a.L);
+                                const uint32_t st = unit_state<KV>(wr[i][g], q0 + b, a.L);
                                 uint32_t off = (st << kLog) + negbase;  // wraps below the part
                                 off = off < dummy ? off : dummy;
                                 load_row<V>(c[b], reinterpret_cast<const char *>(tab) + off);
@@ -406,6 +421,248 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_generic_kernel(GemvArgs a) 
     }
 }
 
+// Decode kernel: the units above, flattened over the matrix (unit g = r * upr + u, row r,
+// unit u of the row).  A workgroup of THREADS threads takes a contiguous range of units in
+// tiles of THREADS * RT; thread t holds units t0 + THREADS i + t (i < RT) of a tile: their
+// stream registers and the bit patterns of their S V decoded values.  For each codebook
+// part in LDS (PART_BYTES at most), every step reads the row at its clamped offset (the
+// row of zeros when the state lies outside the part) and ORs it into its value: every pass
+// but one ORs in zero bits, so each value ends as the table's float copied bit for bit
+// (-0.0 included).  After the last part the unit's S V values, consecutive in the row, are
+// stored: through LDS in runs of 1 KiB per wave where the rows are contiguous (ldo = N),
+// else 16 bytes at a time where the layout allows.
+constexpr int kDecThreads = 1024;
+constexpr int kDecPartBytes = 128 << 10;
+constexpr int kDecWgPerCu = 1;     // workgroups resident per compute unit (LDS-bound)
+constexpr int kDecRegBudget = 80;  // registers for a tile's values and stream registers
+
+template <int KV, int V>
+struct DecShape {
+    static constexpr int U = KV / gcd_c(KV, 32);
+    static constexpr int S = 32 * U / KV;
+    static constexpr int NR = 2 * U;
+    static constexpr int kB = 8 / V;  // table reads in flight per thread
+    static constexpr int B = kB < S ? kB : S;
+    // (units of 32 or more values run one per thread: two spill)
+    static constexpr int kFit =
+        (S * V >= 32 ? 1 : (kDecRegBudget - B * V) / (S * V + NR + 2));
+    static constexpr int RT = kFit < 1 ? 1 : (kFit > 4 ? 4 : kFit);
+};
+
+struct DecArgs {
+    const uint32_t *bits;
+    const uint32_t *s0;
+    const float *C;
+    float *out;
+    int64_t ldo;
+    int64_t bpr;           // blocks per row
+    int nwords;            // stream words per block
+    uint32_t upb;          // units per block
+    uint32_t upr;          // units per row
+    uint32_t units;        // units of the matrix, M * upr
+    uint32_t units_per_wg;
+    int L;
+    int part_log2;
+    int parts;
+    int c_aligned;         // C is 16-byte aligned and a part is whole float4s
+    int vec_out;           // every unit's values start 16-byte aligned
+    int dense;             // vec_out and ldo == N: unit g's values start at out + g S V
+};
+
+// The thread index, recomputed where it is used: the part copies' addresses are then not
+// kept in registers across the tile.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Stream words w_0 .. w_U of unit u (zeros past the range) and the offset in out of its
+// SV values (-1 past the range).
+template <int U, int SV>
+__device__ __forceinline__ void dec_unit_words(const DecArgs &a, uint32_t u, uint32_t u_end,
+                                               uint32_t (&w)[U + 1], int64_t &dst) {
+    dst = -1;
+    if (u < u_end) {
+        const uint32_t row = u / a.upr;
+        const uint32_t uir = u - row * a.upr;
+        const uint32_t bir = uir / a.upb;
+        const uint32_t ju = uir - bir * a.upb;
+        const int64_t blk = static_cast<int64_t>(row) * a.bpr + bir;
+        const uint32_t *wb = a.bits + blk * a.nwords + ju * U;
+        w[0] = ju ? wb[-1] : a.s0[blk];
+#pragma unroll
+        for (int j = 0; j < U; ++j) w[j + 1] = wb[j];
+        dst = static_cast<int64_t>(row) * a.ldo + static_cast<int64_t>(uir) * SV;
+    } else {
+#pragma unroll
+        for (int j = 0; j <= U; ++j) w[j] = 0u;
+    }
+}
+
+template <int KV, int V, int THREADS, int PART_BYTES>
+__global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_cols_kernel(
+    DecArgs a) {
+    using Sh = DecShape<KV, V>;
+    constexpr int U = Sh::U, S = Sh::S, NR = Sh::NR, RT = Sh::RT;
+    constexpr int kLog = log2_row_bytes<V>();
+    static_assert(PART_BYTES / 16 <= 8 * THREADS, "a part is at most 8 float4 per thread");
+    static_assert(THREADS * S * V * 4 <= PART_BYTES, "a tile row's values fit the part space");
+    __shared__ float tab[PART_BYTES / 4 + 4];  // a table part, then one row of zeros
+    const int tid = threadIdx.x;
+    const int64_t per_part = int64_t{1} << a.part_log2;
+    const uint32_t dummy = static_cast<uint32_t>(per_part) << kLog;
+    const int64_t nfl = per_part * V;
+    const int64_t n4 = nfl / 4;
+    const bool vec = a.c_aligned && n4 <= 8 * THREADS;
+
+    const uint32_t u_begin = blockIdx.x * a.units_per_wg;
+    const uint32_t u_end = u_begin + a.units_per_wg < a.units ? u_begin + a.units_per_wg
+                                                              : a.units;
+    for (uint32_t t0 = u_begin; t0 < u_end; t0 += THREADS * RT) {
+        uint32_t wr[RT][NR];
+        uint32_t val[RT][S][V];  // bit patterns of the decoded values
+        int64_t dst[RT];         // offset of the unit's first value in out
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            uint32_t w[U + 1];
+            dec_unit_words<U, S * V>(a, t0 + i * THREADS + tid, u_end, w, dst[i]);
+            unit_regs<U>(wr[i], w);
+#pragma unroll
+            for (int q = 0; q < S; ++q)
+#pragma unroll
+                for (int v = 0; v < V; ++v) val[i][q][v] = 0u;
+        }
+        __syncthreads();  // the previous tile is done with the table
+        col_copy_part<V, THREADS>(tab, vec, a.C, 0, nfl, n4, opaque(tid));
+        __syncthreads();
+        for (int p = 0; p < a.parts; ++p) {
+            uint32_t negbase = 0u - static_cast<uint32_t>(p) * dummy;  // - part start
+            asm volatile("" : "+s"(negbase));
+#pragma unroll
+            for (int i = 0; i < RT; ++i)
+#pragma unroll
+                for (int j = 0; j < NR; ++j) asm volatile("" : "+v"(wr[i][j]));
+#pragma unroll
+            for (int i = 0; i < RT; ++i) {
+                // B reads in flight, then their ORs
+#pragma unroll
+                for (int q0 = 0; q0 < S; q0 += Sh::B) {
+                    constexpr int B = Sh::B;
+                    float c[B][V];
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const uint32_t st = unit_state<KV>(wr[i], q0 + b, a.L);
+                        uint32_t off = (st << kLog) + negbase;  // wraps below the part
+                        off = off < dummy ? off : dummy;
+                        load_row<V>(c[b], reinterpret_cast<const char *>(tab) + off);
+                    }
+#pragma unroll
+                    for (int b = 0; b < B; ++b)
+#pragma unroll
+                        for (int v = 0; v < V; ++v) val[i][q0 + b][v] |= __float_as_uint(c[b][v]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if (p + 1 < a.parts) {
+                __syncthreads();  // every wave is done with part p
+                col_copy_part<V, THREADS>(tab, vec, a.C, p + 1, nfl, n4, opaque(tid));
+                __syncthreads();
+            }
+        }
+        constexpr bool kVec = (S * V) % 4 == 0;
+        constexpr int F4 = kVec ? (S * V) / 4 : 1;  // float4 per unit
+        if (kVec && a.dense) {
+            // The units of a tile row are consecutive in out: restage each row's values
+            // through LDS (the table part is done with) so that a wave stores 1 KiB runs.
+            // A unit's float4 c sits in LDS slot j F4 + (c ^ swz(j)): 16 consecutive lanes
+            // then write, and read, 64 different banks.
+#pragma unroll
+            for (int i = 0; i < RT; ++i) {
+                const uint32_t r0 = t0 + i * THREADS;
+                __syncthreads();  // the table, or the previous row's values, are read
+                float4 *st4 = reinterpret_cast<float4 *>(tab);
+                const uint32_t swz_w = (static_cast<uint32_t>(tid) * F4 / 16) & (F4 - 1);
+#pragma unroll
+                for (int f = 0; f < F4; ++f)
+                    st4[tid * F4 + (f ^ swz_w)] =
+                        make_float4(__uint_as_float(val[i][(4 * f) / V][(4 * f) % V]),
+                                    __uint_as_float(val[i][(4 * f + 1) / V][(4 * f + 1) % V]),
+                                    __uint_as_float(val[i][(4 * f + 2) / V][(4 * f + 2) % V]),
+                                    __uint_as_float(val[i][(4 * f + 3) / V][(4 * f + 3) % V]));
+                __syncthreads();
+                if (r0 < u_end) {
+                    const uint32_t nun = u_end - r0 < THREADS ? u_end - r0 : THREADS;
+                    float4 *o4 = reinterpret_cast<float4 *>(a.out + static_cast<int64_t>(r0) *
+                                                                        (S * V));
+#pragma unroll
+                    for (int f = 0; f < F4; ++f) {
+                        const uint32_t pidx = f * THREADS + tid;  // float4 of the row
+                        const uint32_t j = pidx / F4, c = pidx % F4;
+                        const uint32_t swz = (j * F4 / 16) & (F4 - 1);
+                        if (pidx < nun * F4) o4[pidx] = st4[j * F4 + (c ^ swz)];
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RT; ++i) {
+                float *o = a.out + dst[i];
+                if (dst[i] >= 0 && kVec && a.vec_out) {
+#pragma unroll
+                    for (int f = 0; f < (kVec ? S * V : 0); f += 4)
+                        *reinterpret_cast<float4 *>(o + f) =
+                            make_float4(__uint_as_float(val[i][f / V][f % V]),
+                                        __uint_as_float(val[i][(f + 1) / V][(f + 1) % V]),
+                                        __uint_as_float(val[i][(f + 2) / V][(f + 2) % V]),
+                                        __uint_as_float(val[i][(f + 3) / V][(f + 3) % V]));
+                } else if (dst[i] >= 0) {
+#pragma unroll
+                    for (int q = 0; q < S; ++q)
+#pragma unroll
+                        for (int v = 0; v < V; ++v) o[q * V + v] = __uint_as_float(val[i][q][v]);
+                }
+            }
+        }
+    }
+}
+
+// Any other shape: one workgroup per coding block, one thread per step, the codebook read
+// from global memory.
+// s_t is the L-bit window of s_0 || b_1 || ... || b_n that ends with chunk b_t.
+__device__ __forceinline__ uint32_t stream_bits(const uint32_t *words, int nwords, int pos,
+                                                int nbits) {
+    const int wi = pos >> 5;
+    const uint64_t hi = words[wi];
+    const uint64_t lo = (wi + 1 < nwords) ? words[wi + 1] : 0u;
+    const uint64_t both = (hi << 32) | lo;
+    const int shift = 64 - (pos & 31) - nbits;
+    return static_cast<uint32_t>((both >> shift) & ((uint64_t{1} << nbits) - 1));
+}
+
+__global__ __launch_bounds__(256) void decode_kernel(
+    const uint32_t *__restrict__ bitstream, const uint32_t *__restrict__ start_state,
+    const float *__restrict__ C, int64_t blocks_per_row, int L, int kv, int V, int n,
+    int nwords, float *__restrict__ out, int64_t ldo) {
+    const int64_t blk = blockIdx.x;
+    const int64_t row = blk / blocks_per_row;
+    const int64_t col = blk % blocks_per_row;
+    const uint32_t *words = bitstream + blk * nwords;
+    const uint32_t s0 = start_state[blk];
+    const uint32_t mask = (L >= 32) ? 0xFFFFFFFFu : ((1u << L) - 1u);
+    float *o = out + row * ldo + col * static_cast<int64_t>(n) * V;
+    for (int t = 1 + threadIdx.x; t <= n; t += blockDim.x) {
+        const int P = t * kv;  // stream bits consumed after chunk t
+        uint32_t s;
+        if (P >= L) {
+            s = stream_bits(words, nwords, P - L, L);
+        } else {
+            s = ((s0 << P) | stream_bits(words, nwords, 0, P)) & mask;
+        }
+        for (int v = 0; v < V; ++v) o[(t - 1) * V + v] = C[static_cast<int64_t>(s) * V + v];
+    }
+}
+
+
 // Raise a kernel's dynamic LDS limit to the most this file uses, once per kernel (the
 // attribute is process-wide, so later launches skip the runtime call).  Calls may come
 // from several host threads at once.
@@ -438,6 +695,87 @@ int cu_count() {
 }
 
 }  // namespace
+
+hipError_t launch_decode(const uint32_t *bitstream, const uint32_t *start_state,
+                         const float *C, int64_t M, int64_t N, int L, int k, int V, int T,
+                         float *out, int64_t ldo, hipStream_t s) {
+    const int64_t per_row = N / T;
+    const int64_t nblocks = M * per_row;
+    if (nblocks <= 0) return hipSuccess;
+    const int kv = k * V;
+    const int nwords = (k * T + 31) / 32;
+    const int n = T / V;
+    // Units kernel: every block a whole number of units, and unit indices within 32 bits.
+    const int U = kv / gcd_c(kv, 32);
+    const bool whole = (nwords % U == 0) &&
+                       (static_cast<int64_t>(kv) * n == static_cast<int64_t>(nwords) * 32);
+    const int64_t upr = whole ? per_row * (nwords / U) : 0;
+    if (whole && (V == 1 || V == 2 || V == 4) && M * upr + kDecThreads * 8 < (int64_t{1} << 32)) {
+        DecArgs a{};
+        a.bits = bitstream;
+        a.s0 = start_state;
+        a.C = C;
+        a.out = out;
+        a.ldo = ldo;
+        a.bpr = per_row;
+        a.nwords = nwords;
+        a.upb = static_cast<uint32_t>(nwords / U);
+        a.upr = static_cast<uint32_t>(upr);
+        a.units = static_cast<uint32_t>(M * upr);
+        a.L = L;
+        int plog = L;
+        while ((int64_t{1} << plog) * V * 4 > kDecPartBytes) --plog;
+        a.part_log2 = plog;
+        a.parts = 1 << (L - plog);
+        a.c_aligned = ((reinterpret_cast<uintptr_t>(C) & 15) == 0 &&
+                       ((int64_t{1} << plog) * V) % 4 == 0) ? 1 : 0;
+        const int S = 32 * U / kv;
+        a.vec_out = ((S * V) % 4 == 0 && ldo % 4 == 0 &&
+                     (reinterpret_cast<uintptr_t>(out) & 15) == 0) ? 1 : 0;
+        a.dense = (a.vec_out && ldo == N) ? 1 : 0;
+        const void *kern = nullptr;
+        int rt = 0;
+#define TCQ_DEC_CASE(KV_, V_)                                                              \
+    if (kv == KV_ && V == V_) {                                                           \
+        kern = reinterpret_cast<const void *>(                                            \
+            decode_cols_kernel<KV_, V_, kDecThreads, kDecPartBytes>);                     \
+        rt = DecShape<KV_, V_>::RT;                                                       \
+    }
+        TCQ_DEC_CASE(1, 1)
+        TCQ_DEC_CASE(2, 1)
+        TCQ_DEC_CASE(2, 2)
+        TCQ_DEC_CASE(3, 1)
+        TCQ_DEC_CASE(4, 1)
+        TCQ_DEC_CASE(4, 2)
+        TCQ_DEC_CASE(4, 4)
+        TCQ_DEC_CASE(6, 1)
+        TCQ_DEC_CASE(6, 2)
+        TCQ_DEC_CASE(8, 1)
+        TCQ_DEC_CASE(8, 2)
+        TCQ_DEC_CASE(8, 4)
+#undef TCQ_DEC_CASE
+        if (kern) {
+            const int64_t tile = static_cast<int64_t>(kDecThreads) * rt;
+            const int64_t units = a.units;
+            int64_t grid = (units + tile - 1) / tile;
+            const int64_t slots = cu_count() * kDecWgPerCu;
+            if (grid > slots) grid = slots;
+            a.units_per_wg = static_cast<uint32_t>((units + grid - 1) / grid);
+            grid = (units + a.units_per_wg - 1) / a.units_per_wg;
+            void *args[] = {&a};  // (the kernel's LDS is static)
+            hipError_t e = hipLaunchKernel(kern, dim3(static_cast<unsigned>(grid)),
+                                           dim3(kDecThreads), args, 0, s);
+            if (e != hipSuccess) return e;
+            return hipGetLastError();
+        }
+    }
+
+    const int threads = n >= 256 ? 256 : (n >= 64 ? ((n + 63) / 64) * 64 : 64);
+    // grid.x limit is 2^31-1 blocks; the validated sizes stay far below it
+    hipLaunchKernelGGL(decode_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(threads), 0, s,
+                       bitstream, start_state, C, per_row, L, k * V, V, n, nwords, out, ldo);
+    return hipGetLastError();
+}
 
 hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_state,
                               const float *C, const float *x, float *y, int64_t M, int64_t N,

@@ -182,40 +182,6 @@ __global__ __launch_bounds__(64) void traceback_planes_kernel(
     }
 }
 
-// s_t is the L-bit window of s_0 || b_1 || ... || b_n that ends with chunk b_t.
-__device__ __forceinline__ uint32_t stream_bits(const uint32_t *words, int nwords, int pos,
-                                                int nbits) {
-    const int wi = pos >> 5;
-    const uint64_t hi = words[wi];
-    const uint64_t lo = (wi + 1 < nwords) ? words[wi + 1] : 0u;
-    const uint64_t both = (hi << 32) | lo;
-    const int shift = 64 - (pos & 31) - nbits;
-    return static_cast<uint32_t>((both >> shift) & ((uint64_t{1} << nbits) - 1));
-}
-
-__global__ __launch_bounds__(256) void decode_kernel(
-    const uint32_t *__restrict__ bitstream, const uint32_t *__restrict__ start_state,
-    const float *__restrict__ C, int64_t blocks_per_row, int L, int kv, int V, int n,
-    int nwords, float *__restrict__ out, int64_t ldo) {
-    const int64_t blk = blockIdx.x;
-    const int64_t row = blk / blocks_per_row;
-    const int64_t col = blk % blocks_per_row;
-    const uint32_t *words = bitstream + blk * nwords;
-    const uint32_t s0 = start_state[blk];
-    const uint32_t mask = (L >= 32) ? 0xFFFFFFFFu : ((1u << L) - 1u);
-    float *o = out + row * ldo + col * static_cast<int64_t>(n) * V;
-    for (int t = 1 + threadIdx.x; t <= n; t += blockDim.x) {
-        const int P = t * kv;  // stream bits consumed after chunk t
-        uint32_t s;
-        if (P >= L) {
-            s = stream_bits(words, nwords, P - L, L);
-        } else {
-            s = ((s0 << P) | stream_bits(words, nwords, 0, P)) & mask;
-        }
-        for (int v = 0; v < V; ++v) o[(t - 1) * V + v] = C[static_cast<int64_t>(s) * V + v];
-    }
-}
-
 template <bool W, bool LDS>
 hipError_t launch_one(const Problem &p, const Plan &pl, const float *Wm, const float *d,
                       const float *C, int64_t block0, int64_t nb, char *ws, float *cost,
@@ -264,20 +230,6 @@ hipError_t launch_traceback_planes(const Problem &p, const Plan &pl, int64_t blo
     hipLaunchKernelGGL(traceback_planes_kernel, dim3(static_cast<unsigned>(nb)), dim3(64), 0,
                        s, bp, static_cast<int64_t>(pl.bp_bytes / 8), send, p.L, p.kv, p.n,
                        nwords, block0, bitstream, start_state);
-    return hipGetLastError();
-}
-
-hipError_t launch_decode(const uint32_t *bitstream, const uint32_t *start_state,
-                         const float *C, int64_t M, int64_t N, int L, int k, int V, int T,
-                         float *out, int64_t ldo, hipStream_t s) {
-    const int64_t per_row = N / T;
-    const int64_t nblocks = M * per_row;
-    const int nwords = (k * T + 31) / 32;
-    const int n = T / V;
-    const int threads = n >= 256 ? 256 : (n >= 64 ? ((n + 63) / 64) * 64 : 64);
-    // grid.x limit is 2^31-1 blocks; the validated sizes stay far below it
-    hipLaunchKernelGGL(decode_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(threads), 0, s,
-                       bitstream, start_state, C, per_row, L, k * V, V, n, nwords, out, ldo);
     return hipGetLastError();
 }
 
