@@ -370,6 +370,68 @@ def decode_bench(torch, _lib, w, enc, Ct, iters):
             "frac_hbm": gbps / HBM_PEAK_GBPS, "weights_per_s": w.weights / (us / 1e6)}
 
 
+def decode_shapes_bench(torch, _lib, iters):
+    """tcq_decode on the two 8B-class MLP shapes (14336 x 4096 at k = 2, V = 2 and
+    4096 x 14336 at k = 3), on seeded random bitstreams, into a dense M x N buffer."""
+    out = []
+    for M, N, L, k, V, T in ((14336, 4096, 16, 2, 2, 256), (4096, 14336, 16, 3, 1, 256)):
+        g = torch.Generator(device="cpu").manual_seed(M + N + k)
+        nb = M * (N // T)
+        nw = (k * T + 31) // 32
+        bits = torch.randint(-2 ** 31, 2 ** 31 - 1, (nb, nw), generator=g,
+                             dtype=torch.int32).cuda()
+        s0 = torch.randint(0, 1 << (L - k * V), (nb,), generator=g, dtype=torch.int32).cuda()
+        C = torch.from_numpy(_lib.tcq_make_codebook(L, V, 3001)).cuda()
+        o = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def call():
+            _lib.tcq_decode(bits.data_ptr(), s0.data_ptr(), C.data_ptr(), M, N, L, k, V, T,
+                            o.data_ptr(), N, stream.cuda_stream)
+
+        for _ in range(3):
+            call()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / iters
+        nbytes = 4 * M * N + (bits.numel() + s0.numel()) * 4
+        gbps = nbytes / (us / 1e6) / 1e9
+        out.append({"shape": f"{M}x{N} L={L} k={k} V={V} T={T}", "us_per_call": us,
+                    "algorithmic_bytes": nbytes, "achieved_GBps": gbps,
+                    "frac_hbm": gbps / HBM_PEAK_GBPS, "weights_per_s": M * N / (us / 1e6)})
+        del bits, s0, o
+    return out
+
+
+def stream_probe_bench(torch, _lib, blocks=2048, super_steps=85):
+    """Ceiling of the L = 16, k*V = 2 forward kernel's codebook stream: its codebook loads
+    alone (tcq_l16_stream_probe), in bytes per clock per compute unit at 2.4 GHz."""
+    from trellis_coded_bit_amd import api
+    ws = api.Workspace(_lib.tcq_l16_stream_probe_bytes(blocks), "cuda")
+    stream = torch.cuda.current_stream()
+    _lib.tcq_l16_stream_probe(blocks, super_steps, ws.ptr, ws.nbytes, stream.cuda_stream,
+                              None, None)
+    times = []
+    for _ in range(3):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)  # torch creates the HIP events at their first record
+        b.record(stream)
+        _lib.tcq_l16_stream_probe(blocks, super_steps, ws.ptr, ws.nbytes, stream.cuda_stream,
+                                  a.cuda_event, b.cuda_event)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = min(times)
+    nbytes = blocks * super_steps * 3 * 65536 * 4
+    return {"blocks": blocks, "super_steps": super_steps, "ms": ms, "bytes": nbytes,
+            "B_per_clk_per_cu": nbytes / (ms / 1e3) / (N_CU * CLOCK_HZ)}
+
+
 class EncodeRun:
     """One workload's inputs resident on the GPU, its outputs and workspace, and a timed
     loop of tcq_encode_timed calls (the forward launch bracketed by HIP events on the
@@ -522,6 +584,14 @@ def main():
     if args.decode_iters > 0:
         log(f"[bench] decode of the encoded matrix, {args.decode_iters} calls", args.quiet)
         result["decode"] = decode_bench(torch, _lib, w, run.out, run.Ct, args.decode_iters)
+        log("[bench] decode on the 8B-class MLP shapes", args.quiet)
+        result["decode_shapes"] = decode_shapes_bench(torch, _lib, max(5, args.decode_iters // 5))
+    if w.L == 16 and w.k * w.V == 2:
+        log("[bench] codebook-stream probe of the forward kernel", args.quiet)
+        probe = stream_probe_bench(torch, _lib)
+        probe["forward_kernel_share"] = (main_sum["codebook_l2_B_per_clk_per_cu"] /
+                                         probe["B_per_clk_per_cu"])
+        result["acs"]["codebook_stream_probe"] = probe
     if args.preprocess_iters > 0:
         log("[bench] pre-processing kernels", args.quiet)
         result["preprocess"] = preprocess_bench(torch, _lib, w, run.Wt, args.preprocess_iters)
@@ -540,6 +610,10 @@ def main():
         oms, oacs = o.timed(steps, 1)
         entry = o.summary(oms, oacs)
         entry["steps"] = steps
+        if args.preprocess_iters > 0 and o.w.index == 2:
+            log("[bench] pre-processing kernels on the 4096 x 4096 weights", args.quiet)
+            entry["preprocess"] = preprocess_bench(torch, _lib, o.w, o.Wt,
+                                                   args.preprocess_iters)
         o.free()
         result.setdefault("workloads", {})[o.w.name] = entry
         if o.w.index == 2:

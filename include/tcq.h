@@ -139,6 +139,24 @@ int tcq_encode_timed(const float *W, int64_t M, int64_t N, int64_t ldw, const fl
                      hipEvent_t acs_begin, hipEvent_t acs_end);
 
 /*
+ * tcq_l16_stream_probe -- measurement support: the codebook loads of the L = 16, k*V = 2
+ * forward kernel (same per-lane offsets, order and loads in flight, one 8-wave workgroup
+ * per block, `super_steps` super-steps of 3 steps per block) with the arithmetic, LDS
+ * traffic and backpointer stores taken out, timed between `start` and `stop` (recorded
+ * on `stream`; either may be NULL).  Each block reads 768 KiB per super-step from an
+ * L2-resident 768 KiB array, so blocks * super_steps * 786432 / elapsed is the rate at which
+ * the L2 delivers that access pattern to the compute units, the ceiling of the forward
+ * kernel's codebook stream (4 bytes per state update).  Values read are not meaningful.
+ *   workspace : device, >= tcq_l16_stream_probe_bytes(blocks) bytes, 256-byte aligned
+ * Errors: TCQ_EINVAL (blocks < 1 or > 2^31 - 1, super_steps < 1, NULL or small
+ * workspace), TCQ_EHIP.
+ */
+size_t tcq_l16_stream_probe_bytes(int64_t blocks);
+int tcq_l16_stream_probe(int64_t blocks, int super_steps, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop);
+
+/*
  * tcq_encode_noalloc -- tcq_encode for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments, outputs and errors as tcq_encode, without the workspace: the library uses a

@@ -17,7 +17,7 @@ FAKE = 0x7F0000001000  # never dereferenced: every call below fails validation f
 def _declared():
     with open(os.path.join(ROOT, "include", "tcq.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"\b(tcq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tcq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_declared_symbols():
@@ -269,3 +269,16 @@ def test_scale_field_argument_checks():
 def ctypes_size():
     import ctypes
     return ctypes.pointer(ctypes.c_size_t(0))
+
+
+def test_stream_probe_argument_checks():
+    lib = _lib.load()
+    E = _lib
+    assert lib.tcq_l16_stream_probe_bytes(0) == 0
+    assert lib.tcq_l16_stream_probe_bytes(2) == 3 * 65536 * 4 + 2 * 512 * 4
+    need = lib.tcq_l16_stream_probe_bytes(4)
+    assert lib.tcq_l16_stream_probe(0, 1, FAKE, need, None, None, None) == E.TCQ_EINVAL
+    assert lib.tcq_l16_stream_probe(4, 0, FAKE, need, None, None, None) == E.TCQ_EINVAL
+    assert lib.tcq_l16_stream_probe(4, 1, None, need, None, None, None) == E.TCQ_EINVAL
+    assert lib.tcq_l16_stream_probe(4, 1, FAKE, need - 1, None, None, None) == E.TCQ_EINVAL
+    assert lib.tcq_l16_stream_probe(4, 1, FAKE + 8, need, None, None, None) == E.TCQ_EINVAL

@@ -25,7 +25,8 @@ EXPORTED = ("tcq_version", "tcq_last_error", "tcq_make_codebook",
             "tcq_encode_workspace_bytes", "tcq_encode_workspace_min_bytes", "tcq_encode",
             "tcq_encode_timed", "tcq_encode_noalloc", "tcq_decode", "tcq_decode_gemv",
             "tcq_ldlq_workspace_bytes", "tcq_encode_ldlq", "tcq_bcjr_workspace_bytes",
-            "tcq_bcjr", "tcq_hadamard", "tcq_scale_field_workspace_bytes", "tcq_scale_field")
+            "tcq_bcjr", "tcq_hadamard", "tcq_scale_field_workspace_bytes", "tcq_scale_field",
+            "tcq_l16_stream_probe_bytes", "tcq_l16_stream_probe")
 
 _lib = None
 
@@ -67,6 +68,10 @@ def load():
                                        vp, vp, i64, vp]
     lib.tcq_decode.restype = i32
     lib.tcq_decode.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, i64, vp]
+    lib.tcq_l16_stream_probe_bytes.restype = sz
+    lib.tcq_l16_stream_probe_bytes.argtypes = [i64]
+    lib.tcq_l16_stream_probe.restype = i32
+    lib.tcq_l16_stream_probe.argtypes = [i64, i32, vp, sz, vp, vp, vp]
     lib.tcq_decode_gemv.restype = i32
     lib.tcq_decode_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, vp, vp]
     lib.tcq_ldlq_workspace_bytes.restype = i32
@@ -152,6 +157,17 @@ def tcq_encode_noalloc(W: int, M: int, N: int, ldw: int, d: int | None, codebook
     _check("tcq_encode_noalloc",
            load().tcq_encode_noalloc(W, M, N, ldw, d or None, codebook, L, k, V, T, bitstream,
                                      start_state, cost, recon or None, ldr, stream or None))
+
+
+def tcq_l16_stream_probe_bytes(blocks: int) -> int:
+    return int(load().tcq_l16_stream_probe_bytes(blocks))
+
+
+def tcq_l16_stream_probe(blocks: int, super_steps: int, workspace: int, workspace_bytes: int,
+                         stream: int | None, start: int | None, stop: int | None) -> None:
+    _check("tcq_l16_stream_probe",
+           load().tcq_l16_stream_probe(blocks, super_steps, workspace, workspace_bytes,
+                                       stream or None, start or None, stop or None))
 
 
 def tcq_decode(bitstream: int, start_state: int, codebook: int, M: int, N: int, L: int,

@@ -397,6 +397,50 @@ __global__ __launch_bounds__(64) void traceback_l16_kernel(
 
 constexpr size_t kLdsBytes = kLdsDwords * sizeof(float);
 
+// Codebook-stream ceiling of the forward kernel: the same codebook loads (descriptor,
+// offsets, order, ring of kRing<false> loads in flight, one 8-wave workgroup per block) with
+// the arithmetic, LDS traffic and backpointer stores taken out.  Each lane folds what it
+// loads into one word (one xor per loaded dword, so every load stays live) and stores it
+// at the end.  Its rate of codebook bytes is what the L2 delivers to the compute units
+// for this access pattern: 4 bytes per state update of the forward kernel.
+template <int K>
+__device__ __forceinline__ void probe_position(float4 (&ring)[kRing<false>],
+                                               __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                               uint32_t &x) {
+    constexpr int D = kRing<false>;
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    const float4 c = ring[K % D];
+    ring[K % D] = cb_load_pos<K + D>(rs, voff);
+    x ^= __float_as_uint(c.x) ^ __float_as_uint(c.y) ^ __float_as_uint(c.z) ^
+         __float_as_uint(c.w);
+    asm volatile("" : "+v"(x));  // consumed here, not in a tree at the end
+}
+
+template <int... I>
+__device__ __forceinline__ void probe_positions(float4 (&ring)[kRing<false>],
+                                                __amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                                uint32_t &x, std::integer_sequence<int, I...>) {
+    (probe_position<I>(ring, rs, voff, x), ...);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void l16_stream_probe_kernel(const float4 *cb,
+                                                                       int super_steps,
+                                                                       uint32_t *out) {
+    const uint32_t tid = threadIdx.x;
+    const uint32_t wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float4 *>(cb + wu * (kCopy / kWaves)), 0,
+        3 * kCopy * static_cast<int>(sizeof(float4)), 0x00020000);
+    const uint32_t voff = (tid & 63) * static_cast<uint32_t>(sizeof(float4));
+    float4 ring[kRing<false>];
+    ring_fill<0>(ring, rs, voff);
+    uint32_t x = 0;
+    for (int q = 0; q < super_steps; ++q)
+        probe_positions(ring, rs, voff, x, std::make_integer_sequence<int, kPositions>{});
+    out[static_cast<int64_t>(blockIdx.x) * kThreads + tid] = x;
+}
+
 }  // namespace
 
 bool l16_supported(const Problem &p) { return p.L == 16 && p.kv == 2 && p.V == 1; }
@@ -440,6 +484,24 @@ hipError_t launch_acs_l16(const Problem &p, const Plan &pl, const float *W, cons
                            W, p.ldw, d, cb, p.n, p.blocks_per_row, block0, bp, bp_per_block,
                            send, cost);
     }
+    return hipGetLastError();
+}
+
+size_t l16_stream_probe_bytes(int64_t blocks) {
+    return 3 * sizeof(float4) * kCopy + static_cast<size_t>(blocks) * kThreads * 4;
+}
+
+hipError_t launch_l16_stream_probe(int64_t blocks, int super_steps, char *ws, hipStream_t s) {
+    const float4 *cb = reinterpret_cast<const float4 *>(ws);
+    uint32_t *out = reinterpret_cast<uint32_t *>(ws + 3 * sizeof(float4) * kCopy);
+    // the forward kernel's LDS allocation (unused here), so that one workgroup of 8 waves
+    // runs per compute unit, as in the forward kernel
+    const void *kern = reinterpret_cast<const void *>(l16_stream_probe_kernel);
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(kLdsBytes));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(l16_stream_probe_kernel, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), kLdsBytes, s, cb, super_steps, out);
     return hipGetLastError();
 }
 

@@ -296,6 +296,36 @@ extern "C" int tcq_encode_timed(const float *W, int64_t M, int64_t N, int64_t ld
                        acs_begin, acs_end);
 }
 
+extern "C" size_t tcq_l16_stream_probe_bytes(int64_t blocks) {
+    return blocks > 0 ? l16_stream_probe_bytes(blocks) : 0;
+}
+
+extern "C" int tcq_l16_stream_probe(int64_t blocks, int super_steps, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t start, hipEvent_t stop) {
+    clear_error();
+    const char *fn = "tcq_l16_stream_probe";
+    if (blocks < 1 || blocks > 0x7FFFFFFF || super_steps < 1) {
+        set_error("%s: blocks=%lld and super_steps=%d must be positive (blocks < 2^31)", fn,
+                  (long long)blocks, super_steps);
+        return TCQ_EINVAL;
+    }
+    if (!workspace || workspace_bytes < l16_stream_probe_bytes(blocks)) {
+        set_error("%s: workspace of %zu bytes is below %zu", fn,
+                  workspace ? workspace_bytes : size_t{0}, l16_stream_probe_bytes(blocks));
+        return TCQ_EINVAL;
+    }
+    const int rc = check_workspace_alignment(fn, workspace);
+    if (rc != TCQ_OK) return rc;
+    hipError_t e = hipSuccess;
+    if (start) e = hipEventRecord(start, stream);
+    if (e == hipSuccess)
+        e = launch_l16_stream_probe(blocks, super_steps, static_cast<char *>(workspace), stream);
+    if (e == hipSuccess && stop) e = hipEventRecord(stop, stream);
+    if (e != hipSuccess) return hip_fail(fn, "probe launch", e);
+    return TCQ_OK;
+}
+
 extern "C" int tcq_decode(const uint32_t *bitstream, const uint32_t *start_state,
                           const float *codebook, int64_t M, int64_t N, int L, int k, int V,
                           int T, float *out, int64_t ldo, hipStream_t stream) {

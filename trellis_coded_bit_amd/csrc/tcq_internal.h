@@ -63,6 +63,10 @@ hipError_t launch_decode(const uint32_t *bitstream, const uint32_t *start_state,
                          const float *C, int64_t M, int64_t N, int L, int k, int V, int T,
                          float *out, int64_t ldo, hipStream_t s);
 
+// Codebook-stream probe of the L = 16 forward kernel (measurement only).
+size_t l16_stream_probe_bytes(int64_t blocks);
+hipError_t launch_l16_stream_probe(int64_t blocks, int super_steps, char *ws, hipStream_t s);
+
 hipError_t launch_decode_gemv(const uint32_t *bitstream, const uint32_t *start_state,
                               const float *C, const float *x, float *y, int64_t M, int64_t N,
                               int L, int k, int V, int T, hipStream_t s);
