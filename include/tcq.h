@@ -177,8 +177,8 @@ int tcq_encode_noalloc(const float *W, int64_t M, int64_t N, int64_t ldw, const 
                        hipStream_t stream);
 
 /*
- * tcq_decode -- rebuild weights from bitstreams (Pingala-8 post: decoding reads bits,
- * updates the state and looks up values).
+ * tcq_decode -- rebuild weights from bitstreams (Pingala-8 post, decoding paragraph: the
+ * state is a shift register over the chunks, and each state indexes the codebook).
  *   bitstream, start_state : device, as written by tcq_encode for an M x N problem
  *   codebook               : device, 2^L * V floats
  *   out                    : device out, M x N floats with row stride ldo >= N;
@@ -191,7 +191,7 @@ int tcq_decode(const uint32_t *bitstream, const uint32_t *start_state, const flo
 
 /*
  * tcq_decode_gemv -- y = W_hat x with W_hat decoded inside the product (Pingala-8 post,
- * decoding paragraph: decoding is cheap and runs inside the matrix-vector product).
+ * decoding paragraph: the decode is fused into the matrix-vector product).
  *   bitstream, start_state : device, as written by tcq_encode for an M x N problem
  *   codebook               : device, 2^L * V floats
  *   x                      : device, N floats

@@ -1,6 +1,7 @@
-// Decoding (Pingala-8 post, decoding paragraph: decoding reads bits, updates the state and
-// looks values up, also inside the matrix-vector product): W_hat itself (tcq_decode) and
-// y = W_hat x with the weights decoded inside the product (tcq_decode_gemv).
+// Decoding (Pingala-8 post, decoding paragraph): a shift register over the bitstream
+// gives each step's state, and the state indexes the codebook; the same walk can feed a
+// matrix-vector product directly.  Here: W_hat itself (tcq_decode) and y = W_hat x with
+// the weights decoded inside the product (tcq_decode_gemv).
 //
 // The state of step t is the L-bit window of s_0 || b_1 || ... || b_n that ends with
 // chunk b_t, so it can be read straight from two neighbouring 32-bit words of the stream
