@@ -4,7 +4,9 @@ matrix, recommended workspace), checked against the oracle under the bar of pari
 - the 2048 x 2048 and the 4096 x 4096 weighted workloads: every block (the latter in
   four chunks of 16384 blocks, so that progress is printed as it goes);
 - the 4096 x 14336 (k = 3) and 14336 x 4096 (V = 2) workloads: a seeded uniform sample
-  of 8192 blocks plus every block of the first and the last row.
+  of 8192 blocks plus every block of the first and the last row, or every block (14
+  chunks each, about 7 minutes of oracle time on 16 threads) for the workloads listed
+  in TCQ_TEST_FULL_WORKLOADS (e.g. "3,4").
 
 Each case prints its exact / excused / failed block counts."""
 import os
@@ -29,9 +31,17 @@ THREADS = min(16, os.cpu_count() or 1)
 SAMPLE = int(os.environ.get("TCQ_TEST_SAMPLE_BLOCKS", "8192"))
 CHUNK = 16384
 
+FULL = {int(x) for x in os.environ.get("TCQ_TEST_FULL_WORKLOADS", "").split(",") if x.strip()}
+
 # (workload index, chunk): chunk i of a fully checked workload covers blocks
 # [i * CHUNK, (i + 1) * CHUNK); chunk -1 is the sample of a sampled workload.
-CASES = [(1, 0), (2, 0), (2, 1), (2, 2), (2, 3), (3, -1), (4, -1)]
+CASES = [(1, 0), (2, 0), (2, 1), (2, 2), (2, 3)]
+for _i in (3, 4):
+    if _i in FULL:
+        _n = wl.WORKLOADS[_i].blocks
+        CASES += [(_i, c) for c in range((_n + CHUNK - 1) // CHUNK)]
+    else:
+        CASES.append((_i, -1))
 
 _cache = {}
 
