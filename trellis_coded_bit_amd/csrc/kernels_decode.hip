@@ -500,11 +500,12 @@ __device__ __forceinline__ void dec_unit_words(const DecArgs &a, uint32_t u, uin
     }
 }
 
-template <int KV, int V, int THREADS, int PART_BYTES>
+template <int KV, int V, int THREADS, int PART_BYTES, int RT>
 __global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_cols_kernel(
     DecArgs a) {
     using Sh = DecShape<KV, V>;
-    constexpr int U = Sh::U, S = Sh::S, NR = Sh::NR, RT = Sh::RT;
+    constexpr int U = Sh::U, S = Sh::S, NR = Sh::NR;
+    static_assert(RT >= 1 && RT <= Sh::RT, "rows of a tile");
     constexpr int kLog = log2_row_bytes<V>();
     static_assert(PART_BYTES / 16 <= 8 * THREADS, "a part is at most 8 float4 per thread");
     static_assert(THREADS * S * V * 4 <= PART_BYTES, "a tile row's values fit the part space");
@@ -735,11 +736,14 @@ hipError_t launch_decode(const uint32_t *bitstream, const uint32_t *start_state,
                      (reinterpret_cast<uintptr_t>(out) & 15) == 0) ? 1 : 0;
         a.dense = (a.vec_out && ldo == N) ? 1 : 0;
         const void *kern = nullptr;
+        const void *kern1 = nullptr;
         int rt = 0;
 #define TCQ_DEC_CASE(KV_, V_)                                                              \
     if (kv == KV_ && V == V_) {                                                           \
         kern = reinterpret_cast<const void *>(                                            \
-            decode_cols_kernel<KV_, V_, kDecThreads, kDecPartBytes>);                     \
+            decode_cols_kernel<KV_, V_, kDecThreads, kDecPartBytes, DecShape<KV_, V_>::RT>); \
+        kern1 = reinterpret_cast<const void *>(                                           \
+            decode_cols_kernel<KV_, V_, kDecThreads, kDecPartBytes, 1>);                  \
         rt = DecShape<KV_, V_>::RT;                                                       \
     }
         TCQ_DEC_CASE(1, 1)
@@ -756,13 +760,16 @@ hipError_t launch_decode(const uint32_t *bitstream, const uint32_t *start_state,
         TCQ_DEC_CASE(8, 4)
 #undef TCQ_DEC_CASE
         if (kern) {
-            const int64_t tile = static_cast<int64_t>(kDecThreads) * rt;
+            // as many workgroups as fit, each at least one tile row; tiles of one row
+            // where a workgroup has fewer units than a full tile (each tile copies the
+            // whole table into LDS, so rows are only worth adding when there are units)
             const int64_t units = a.units;
-            int64_t grid = (units + tile - 1) / tile;
+            int64_t grid = (units + kDecThreads - 1) / kDecThreads;
             const int64_t slots = cu_count() * kDecWgPerCu;
             if (grid > slots) grid = slots;
             a.units_per_wg = static_cast<uint32_t>((units + grid - 1) / grid);
             grid = (units + a.units_per_wg - 1) / a.units_per_wg;
+            if (a.units_per_wg < static_cast<uint32_t>(kDecThreads * rt)) kern = kern1;
             void *args[] = {&a};  // (the kernel's LDS is static)
             hipError_t e = hipLaunchKernel(kern, dim3(static_cast<unsigned>(grid)),
                                            dim3(kDecThreads), args, 0, s);
