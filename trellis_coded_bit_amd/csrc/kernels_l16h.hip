@@ -99,12 +99,13 @@ __device__ __forceinline__ void ringh_prime(float4 (&ring)[Ring<V>::kSize],
 }
 
 // One group (I-th of segment SEG) of a half-step without metric: the four successors all
-// take the kept predecessor cost.
+// take the kept predecessor cost.  No scheduling barrier between these groups (they load
+// no codebook values), so the compare -> SALU -> carry-in chain of one group overlaps the
+// minimums of the next.
 template <int SEG, int NM, int I>
 __device__ __forceinline__ void acsh_group_plain(uint32_t (&J)[kRegs], uint32_t &acc) {
     constexpr int P = seg_step(SEG);
     constexpr uint32_t g = seg_group(SEG, I);
-    __builtin_amdgcn_sched_barrier(0);
     constexpr int r0 = phys(NM, group_reg(P, g, 0)), r1 = phys(NM, group_reg(P, g, 1));
     constexpr int r2 = phys(NM, group_reg(P, g, 2)), r3 = phys(NM, group_reg(P, g, 3));
     const uint32_t u0 = J[r0], u1 = J[r1], u2 = J[r2], u3 = J[r3];
