@@ -138,8 +138,10 @@ template <int V>
 constexpr int log2_row_bytes() { return V == 1 ? 2 : (V == 2 ? 3 : 4); }
 
 // Part p of the table into LDS, then the row of zeros after it.  With 16-byte aligned
-// parts of at most 8 x 1024 float4, each thread issues its eight loads (the index clamped,
-// so every load is in bounds) before storing them.
+// parts of at most 8 x 1024 float4, each thread loads eight float4 (the index clamped, so
+// every load is in bounds) and stores them.  In the GEMV kernel the compiler issues these
+// loads one at a time (its registers hold a tile's rows); the LDS-direct copy below was
+// still slower there (13.4 against 10.8 us at 2048 x 2048), so it keeps this one.
 template <int V, int THREADS = kColThreads>
 __device__ __forceinline__ void col_copy_part(float *tab, bool vec, const float *C, int p,
                                               int64_t nfl, int64_t n4, int tid) {
@@ -157,6 +159,37 @@ __device__ __forceinline__ void col_copy_part(float *tab, bool vec, const float 
             const int64_t j = static_cast<int64_t>(u) * THREADS + tid;
             if (j < n4) d4[j] = t[u];
         }
+    } else {
+        const float *src = C + static_cast<int64_t>(p) * nfl;
+        for (int64_t j = tid; j < nfl; j += THREADS) tab[j] = src[j];
+    }
+    if (tid < 4) tab[nfl + tid] = 0.0f;
+}
+
+// The same copy for the decode kernel, whose tile values leave no registers for eight
+// float4 loads in flight (the copy above then runs one load at a time): each wave moves
+// its 64-float4 chunks straight from global memory into LDS (global_load_lds_dwordx4: lane
+// i's 16 bytes land at the wave's LDS address + 16 i), all eight chunks in flight, then
+// waits for them.  A chunk that the part does not fill takes the register path.
+template <int V, int THREADS>
+__device__ __forceinline__ void dec_copy_part(float *tab, bool vec, const float *C, int p,
+                                              int64_t nfl, int64_t n4, int tid) {
+    if (vec) {
+        const float4 *s4 = reinterpret_cast<const float4 *>(C + static_cast<int64_t>(p) * nfl);
+        float4 *d4 = reinterpret_cast<float4 *>(tab);
+        const int64_t lane = tid & 63;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t base = static_cast<int64_t>(u) * THREADS + (tid & ~63);
+            if (base + 64 <= n4) {
+                __builtin_amdgcn_global_load_lds(
+                    s4 + base + lane,
+                    (__attribute__((address_space(3))) void *)(d4 + base), 16, 0, 0);
+            } else if (base + lane < n4) {
+                d4[base + lane] = s4[base + lane];
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // the LDS writes of the loads above are done
     } else {
         const float *src = C + static_cast<int64_t>(p) * nfl;
         for (int64_t j = tid; j < nfl; j += THREADS) tab[j] = src[j];
@@ -535,7 +568,7 @@ __global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_c
                 for (int v = 0; v < V; ++v) val[i][q][v] = 0u;
         }
         __syncthreads();  // the previous tile is done with the table
-        col_copy_part<V, THREADS>(tab, vec, a.C, 0, nfl, n4, opaque(tid));
+        dec_copy_part<V, THREADS>(tab, vec, a.C, 0, nfl, n4, opaque(tid));
         __syncthreads();
         for (int p = 0; p < a.parts; ++p) {
             uint32_t negbase = 0u - static_cast<uint32_t>(p) * dummy;  // - part start
@@ -567,7 +600,7 @@ __global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_c
             }
             if (p + 1 < a.parts) {
                 __syncthreads();  // every wave is done with part p
-                col_copy_part<V, THREADS>(tab, vec, a.C, p + 1, nfl, n4, opaque(tid));
+                dec_copy_part<V, THREADS>(tab, vec, a.C, p + 1, nfl, n4, opaque(tid));
                 __syncthreads();
             }
         }
