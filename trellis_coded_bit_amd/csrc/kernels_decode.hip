@@ -138,55 +138,31 @@ template <int V>
 constexpr int log2_row_bytes() { return V == 1 ? 2 : (V == 2 ? 3 : 4); }
 
 // Part p of the table into LDS, then the row of zeros after it.  With 16-byte aligned
-// parts of at most 8 x 1024 float4, each thread loads eight float4 (the index clamped, so
-// every load is in bounds) and stores them.  In the GEMV kernel the compiler issues these
-// loads one at a time (its registers hold a tile's rows); the LDS-direct copy below was
-// still slower there (13.4 against 10.8 us at 2048 x 2048), so it keeps this one.
-template <int V, int THREADS = kColThreads>
-__device__ __forceinline__ void col_copy_part(float *tab, bool vec, const float *C, int p,
-                                              int64_t nfl, int64_t n4, int tid) {
-    if (vec) {
-        const float4 *s4 = reinterpret_cast<const float4 *>(C + static_cast<int64_t>(p) * nfl);
-        float4 *d4 = reinterpret_cast<float4 *>(tab);
-        float4 t[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t j = static_cast<int64_t>(u) * THREADS + tid;
-            t[u] = s4[j < n4 ? j : n4 - 1];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int64_t j = static_cast<int64_t>(u) * THREADS + tid;
-            if (j < n4) d4[j] = t[u];
-        }
-    } else {
-        const float *src = C + static_cast<int64_t>(p) * nfl;
-        for (int64_t j = tid; j < nfl; j += THREADS) tab[j] = src[j];
-    }
-    if (tid < 4) tab[nfl + tid] = 0.0f;
-}
-
-// The same copy for the decode kernel, whose tile values leave no registers for eight
-// float4 loads in flight (the copy above then runs one load at a time): each wave moves
-// its 64-float4 chunks straight from global memory into LDS (global_load_lds_dwordx4: lane
-// i's 16 bytes land at the wave's LDS address + 16 i), all eight chunks in flight, then
-// waits for them.  A chunk that the part does not fill takes the register path.
+// parts of at most 8 x THREADS float4, each wave moves its 64-float4 chunks straight from
+// global memory into LDS (buffer_load_dwordx4 ... lds: lane i's 16 bytes land at the
+// chunk's LDS address + 16 i), all eight in flight, then waits for them.  The buffer's
+// range ends with the part, so the lanes of a chunk that runs past it load zeros (into
+// LDS inside the 8 x THREADS float4, where the row of zeros goes anyway).  One VGPR of
+// offset serves every load.  Copied through registers instead, the loads of a thread went
+// out one at a time (the registers hold a tile's values), and the 64-bit addresses of
+// per-lane LDS-direct loads made the GEMV kernel spill.
 template <int V, int THREADS>
-__device__ __forceinline__ void dec_copy_part(float *tab, bool vec, const float *C, int p,
-                                              int64_t nfl, int64_t n4, int tid) {
+__device__ __forceinline__ void copy_part(float *tab, bool vec, const float *C, int p,
+                                          int64_t nfl, int64_t n4, int tid) {
     if (vec) {
-        const float4 *s4 = reinterpret_cast<const float4 *>(C + static_cast<int64_t>(p) * nfl);
-        float4 *d4 = reinterpret_cast<float4 *>(tab);
-        const int64_t lane = tid & 63;
+        const float *part = C + static_cast<int64_t>(p) * nfl;
+        const int wb = tid & ~63;  // the wave's first thread
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int64_t base = static_cast<int64_t>(u) * THREADS + (tid & ~63);
-            if (base + 64 <= n4) {
-                __builtin_amdgcn_global_load_lds(
-                    s4 + base + lane,
-                    (__attribute__((address_space(3))) void *)(d4 + base), 16, 0, 0);
-            } else if (base + lane < n4) {
-                d4[base + lane] = s4[base + lane];
+            const int base = u * THREADS + wb;  // float4 index of the wave's chunk
+            if (base < n4) {
+                // float4 u THREADS .. n4 - 1 of the part; the lane offset is range-checked
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float *>(part + 4 * u * THREADS), 0,
+                    static_cast<int>((n4 - u * THREADS) * 16), 0x00020000);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void *)(tab + 4 * base), 16, tid * 16,
+                    0, 0, 0);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);  // the LDS writes of the loads above are done
@@ -330,7 +306,7 @@ __global__ __launch_bounds__(kColThreads) void gemv_cols_kernel(ColArgs a) {
             }
         }
         __syncthreads();  // the previous tile is done with the table and the row sums
-        col_copy_part<V>(tab, vec, a.C, 0, nfl, n4, tid);
+        copy_part<V, kColThreads>(tab, vec, a.C, 0, nfl, n4, tid);
         __syncthreads();
         for (int p = 0; p < a.parts; ++p) {
             uint32_t negbase = 0u - static_cast<uint32_t>(p) * dummy;  // - part start
@@ -371,7 +347,7 @@ __global__ __launch_bounds__(kColThreads) void gemv_cols_kernel(ColArgs a) {
             }
             if (p + 1 < a.parts) {
                 __syncthreads();  // every wave is done with part p
-                col_copy_part<V>(tab, vec, a.C, p + 1, nfl, n4, tid);
+                copy_part<V, kColThreads>(tab, vec, a.C, p + 1, nfl, n4, tid);
                 __syncthreads();
             }
         }
@@ -568,7 +544,7 @@ __global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_c
                 for (int v = 0; v < V; ++v) val[i][q][v] = 0u;
         }
         __syncthreads();  // the previous tile is done with the table
-        dec_copy_part<V, THREADS>(tab, vec, a.C, 0, nfl, n4, opaque(tid));
+        copy_part<V, THREADS>(tab, vec, a.C, 0, nfl, n4, opaque(tid));
         __syncthreads();
         for (int p = 0; p < a.parts; ++p) {
             uint32_t negbase = 0u - static_cast<uint32_t>(p) * dummy;  // - part start
@@ -600,7 +576,7 @@ __global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_c
             }
             if (p + 1 < a.parts) {
                 __syncthreads();  // every wave is done with part p
-                dec_copy_part<V, THREADS>(tab, vec, a.C, p + 1, nfl, n4, opaque(tid));
+                copy_part<V, THREADS>(tab, vec, a.C, p + 1, nfl, n4, opaque(tid));
                 __syncthreads();
             }
         }
