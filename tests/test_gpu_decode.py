@@ -77,6 +77,11 @@ CASES = [
     (15, 4, 2, 64, 5, 256, None),        # k*V = 8, V = 2
     (9, 2, 1, 100, 6, 300, None),        # block not a whole number of units: per-block kernel
     (8, 3, 1, 10, 4, 40, 41),            # 30-bit blocks: per-block kernel
+    # tables smaller than one wave's 64-float4 chunk of the part copy (lanes past the
+    # table load zeros) and exactly one chunk
+    (6, 2, 1, 64, 9, 256, None),         # 16 float4
+    (5, 1, 4, 32, 6, 128, None),         # 32 float4, V = 4
+    (7, 1, 2, 64, 5, 256, None),         # 64 float4
 ]
 
 
