@@ -9,9 +9,10 @@ Prints one JSON line (rank 0).  Alongside the throughput it reports the forward
 kernel's roofline -- VALU-bound: algorithmic issue slots per state update (packed fp32
 counting one slot) over 256 CUs x 64 slots x 2.4 GHz, the launch timed live with HIP
 events on its stream -- and the CPU oracle timed on a bounded sample of the same
-workload on this host.  It also times the encode of the 4096 x 4096 weighted workload
-('weighted'), tcq_decode and the fused decode + GEMV on the encoded matrix, the
-pre-processing kernels, the soft trellis and the error-feedback driver.
+workload on this host.  It also times the encode of the other workloads ('workloads';
+the 4096 x 4096 weighted one also as 'weighted'), tcq_decode and the fused decode + GEMV
+on the encoded matrix, the pre-processing kernels, the soft trellis and the
+error-feedback driver.
 """
 from __future__ import annotations
 
@@ -72,9 +73,10 @@ def parse():
                     help="calls of the fused decode+GEMV timed after the encoder (0: skip)")
     ap.add_argument("--decode-iters", type=int, default=50,
                     help="calls of tcq_decode timed after the encoder (0: skip)")
-    ap.add_argument("--also", default="2",
+    ap.add_argument("--also", default="0,2,3,4",
                     help="comma-separated workloads whose encode is also timed (3 or 5 "
-                         "steps each); workload 2 is reported as 'weighted'")
+                         "steps each, under 'workloads'); workload 2 is also reported as "
+                         "'weighted'")
     ap.add_argument("--preprocess-iters", type=int, default=100,
                     help="timed calls of the Hadamard and scale-field kernels (0: skip)")
     ap.add_argument("--bcjr-tau", type=float, default=0.1,
