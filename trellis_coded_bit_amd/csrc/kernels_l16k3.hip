@@ -77,12 +77,14 @@ __device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b 
 // One group (I-th of segment SEG) under naming NM: 8-way minimum with the lowest index
 // on ties, three backpointer bits shifted in.  The minimum takes four VALU minimums
 // (three of them v_min3); seven equality compares against it give masks e0 .. e6, and
-// the index of the first set mask is assembled on the SALU:
-//   bit 2 = no match among 0..3;  bit 1 = first match in 2..3, or none in 0..5;
+// the index j of the first set mask is assembled on the SALU (13 operations):
+//   bit 2 of j = no match among 0..3;  bit 1 = first match in 2..3, or none in 0..5;
 //   bit 0 = none of: e0, e2 without e0|e1, e4 without a match in 0..3, e6 without one
 //           in 0..5.
-// (A tournament of pairwise minimums and strict compares gives the same index with
-// three more VALU operations per group; it ran 2 % slower at 4096 x 14336.)
+// Bit 2 is stored inverted (the mask "a match among 0..3" as it is, one operation fewer)
+// and the traceback flips it back.  (A tournament of pairwise minimums and strict
+// compares gives the same index with three more VALU operations per group; it ran 2 %
+// slower at 4096 x 14336, and storing bit 2 as it is 1 % slower.)
 template <int SEG, bool WEIGHTED, int NM, int I>
 __device__ __forceinline__ void acs3_group(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch3],
                                            __amdgpu_buffer_rsrc_t rs, uint32_t voff, float wt,
@@ -108,12 +110,12 @@ __device__ __forceinline__ void acs3_group(uint32_t (&J)[kRegs], float4 (&ring)[
     const uint64_t e2 = __ballot(u2 == mu), e3 = __ballot(u3 == mu);
     const uint64_t e4 = __ballot(u4 == mu), e5 = __ballot(u5 == mu);
     const uint64_t e6 = __ballot(u6 == mu);
-    const uint64_t t01 = e0 | e1, t45 = e4 | e5;
-    const uint64_t top = ~(t01 | (e2 | e3));
-    const uint64_t y = top & ~t45;
-    const uint64_t b1 = ((e2 | e3) & ~t01) | y;
-    const uint64_t b0 = ~((e0 | (e2 & ~t01)) | ((e4 & top) | (e6 & y)));
-    acc = shift_in(shift_in(shift_in(acc, top), b1), b0);
+    const uint64_t t01 = e0 | e1, t23 = e2 | e3, t45 = e4 | e5;
+    const uint64_t a03 = t01 | t23;  // a match among 0..3: index bit 2 clear
+    const uint64_t y = ~(a03 | t45);
+    const uint64_t b1 = (t23 & ~t01) | y;
+    const uint64_t b0 = ~((e0 | (e2 & ~t01)) | ((e4 & ~a03) | (e6 & y)));
+    acc = shift_in(shift_in(shift_in(acc, a03), b1), b0);
     const float m = __uint_as_float(mu);
     const float e[8] = {wt - ca.x, wt - ca.y, wt - ca.z, wt - ca.w,
                         wt - cbv.x, wt - cbv.y, wt - cbv.z, wt - cbv.w};
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(64) void traceback_l16k3_kernel(
             const uint32_t g = reg_group3(p, sl.r);
             const uint2 word = bpb[(tt - 1) * kThreads + sl.w * kLanes + sl.l];
             const uint32_t bits = bp3_half(p, g) ? word.y : word.x;
-            jb = (bits >> bp3_shift(p, g)) & 7u;
+            jb = ((bits >> bp3_shift(p, g)) & 7u) ^ 4u;  // bit 2 is stored inverted
         }
         const uint32_t j0 = __builtin_amdgcn_readlane(jb, 0);
         if (lane == 0) chunk[t - 1] = static_cast<uint8_t>(s & 7u);
