@@ -477,6 +477,7 @@ struct DecArgs {
     int c_aligned;         // C is 16-byte aligned and a part is whole float4s
     int vec_out;           // every unit's values start 16-byte aligned
     int dense;             // vec_out and ldo == N: unit g's values start at out + g S V
+    int upb_log2;          // log2(upb) when upb is a power of two, else -1
 };
 
 // The thread index, recomputed where it is used: the part copies' addresses are then not
@@ -486,23 +487,27 @@ __device__ __forceinline__ int opaque(int v) {
     return v;
 }
 
-// Stream words w_0 .. w_U of unit u (zeros past the range) and the offset in out of its
-// SV values (-1 past the range).
+// Stream words w_0 .. w_U of unit u (zeros past the range) and, if need_dst, the offset
+// in out of its SV values (-1 past the range).  Blocks are whole units, so a block's
+// words are its units' words: unit u's U words follow unit u - 1's (at u U), and its
+// block is u / upb (a shift when upb is a power of two); only the row offset in out
+// needs the division by the units per row.
 template <int U, int SV>
 __device__ __forceinline__ void dec_unit_words(const DecArgs &a, uint32_t u, uint32_t u_end,
-                                               uint32_t (&w)[U + 1], int64_t &dst) {
+                                               uint32_t (&w)[U + 1], int64_t &dst,
+                                               bool need_dst) {
     dst = -1;
     if (u < u_end) {
-        const uint32_t row = u / a.upr;
-        const uint32_t uir = u - row * a.upr;
-        const uint32_t bir = uir / a.upb;
-        const uint32_t ju = uir - bir * a.upb;
-        const int64_t blk = static_cast<int64_t>(row) * a.bpr + bir;
-        const uint32_t *wb = a.bits + blk * a.nwords + ju * U;
+        const uint32_t blk = a.upb_log2 >= 0 ? (u >> a.upb_log2) : u / a.upb;
+        const uint32_t ju = u - blk * a.upb;
+        const uint32_t *wb = a.bits + static_cast<int64_t>(u) * U;
         w[0] = ju ? wb[-1] : a.s0[blk];
 #pragma unroll
         for (int j = 0; j < U; ++j) w[j + 1] = wb[j];
-        dst = static_cast<int64_t>(row) * a.ldo + static_cast<int64_t>(uir) * SV;
+        if (need_dst) {
+            const uint32_t row = u / a.upr;
+            dst = static_cast<int64_t>(row) * a.ldo + static_cast<int64_t>(u - row * a.upr) * SV;
+        }
     } else {
 #pragma unroll
         for (int j = 0; j <= U; ++j) w[j] = 0u;
@@ -526,6 +531,7 @@ __global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_c
     const int64_t n4 = nfl / 4;
     const bool vec = a.c_aligned && n4 <= 8 * THREADS;
 
+    const bool need_dst = !((S * V) % 4 == 0 && a.dense);  // the dense stores use none
     const uint32_t u_begin = blockIdx.x * a.units_per_wg;
     const uint32_t u_end = u_begin + a.units_per_wg < a.units ? u_begin + a.units_per_wg
                                                               : a.units;
@@ -536,7 +542,7 @@ __global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_c
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
             uint32_t w[U + 1];
-            dec_unit_words<U, S * V>(a, t0 + i * THREADS + tid, u_end, w, dst[i]);
+            dec_unit_words<U, S * V>(a, t0 + i * THREADS + tid, u_end, w, dst[i], need_dst);
             unit_regs<U>(wr[i], w);
 #pragma unroll
             for (int q = 0; q < S; ++q)
@@ -733,6 +739,9 @@ hipError_t launch_decode(const uint32_t *bitstream, const uint32_t *start_state,
         a.upb = static_cast<uint32_t>(nwords / U);
         a.upr = static_cast<uint32_t>(upr);
         a.units = static_cast<uint32_t>(M * upr);
+        a.upb_log2 = -1;
+        for (int b = 0; b < 31; ++b)
+            if (a.upb == (1u << b)) a.upb_log2 = b;
         a.L = L;
         int plog = L;
         while ((int64_t{1} << plog) * V * 4 > kDecPartBytes) --plog;
