@@ -140,30 +140,30 @@ constexpr int log2_row_bytes() { return V == 1 ? 2 : (V == 2 ? 3 : 4); }
 // Part p of the table into LDS, then the row of zeros after it.  With 16-byte aligned
 // parts of at most 8 x THREADS float4, each wave moves its 64-float4 chunks straight from
 // global memory into LDS (buffer_load_dwordx4 ... lds: lane i's 16 bytes land at the
-// chunk's LDS address + 16 i), all eight in flight, then waits for them.  The buffer's
-// range ends with the part, so the lanes of a chunk that runs past it load zeros (into
-// LDS inside the 8 x THREADS float4, where the row of zeros goes anyway).  One VGPR of
-// offset serves every load.  Copied through registers instead, the loads of a thread went
-// out one at a time (the registers hold a tile's values), and the 64-bit addresses of
-// per-lane LDS-direct loads made the GEMV kernel spill.
+// chunk's LDS address + 16 i), all eight in flight, then waits for them.  One buffer
+// descriptor covers the part and the whole byte offset sits in the range-checked VGPR, so
+// the lanes of a chunk that runs past the part load zeros (into LDS inside the
+// 8 x THREADS float4, where the row of zeros goes anyway).  The chunk's LDS address and
+// its test against the part size are scalar.  Copied through registers instead, the loads
+// of a thread went out one at a time (the registers hold a tile's values), and the 64-bit
+// addresses of per-lane LDS-direct loads made the GEMV kernel spill.
 template <int V, int THREADS>
 __device__ __forceinline__ void copy_part(float *tab, bool vec, const float *C, int p,
                                           int64_t nfl, int64_t n4, int tid) {
     if (vec) {
-        const float *part = C + static_cast<int64_t>(p) * nfl;
-        const int wb = tid & ~63;  // the wave's first thread
+        // one descriptor over the part; the whole offset is in the (range-checked) VGPR
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(C + static_cast<int64_t>(p) * nfl), 0,
+            static_cast<int>(n4 * 16), 0x00020000);
+        const int wb = __builtin_amdgcn_readfirstlane(tid & ~63);  // the wave's first thread
+        const int n4i = static_cast<int>(n4);  // at most 8 x THREADS
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int base = u * THREADS + wb;  // float4 index of the wave's chunk
-            if (base < n4) {
-                // float4 u THREADS .. n4 - 1 of the part; the lane offset is range-checked
-                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                    const_cast<float *>(part + 4 * u * THREADS), 0,
-                    static_cast<int>((n4 - u * THREADS) * 16), 0x00020000);
+            if (base < n4i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (__attribute__((address_space(3))) void *)(tab + 4 * base), 16, tid * 16,
-                    0, 0, 0);
-            }
+                    rs, (__attribute__((address_space(3))) void *)(tab + 4 * base), 16,
+                    (tid + u * THREADS) * 16, 0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(0);  // the LDS writes of the loads above are done
     } else {
