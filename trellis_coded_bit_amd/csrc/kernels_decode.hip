@@ -137,17 +137,18 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int V>
 constexpr int log2_row_bytes() { return V == 1 ? 2 : (V == 2 ? 3 : 4); }
 
-// Part p of the table into LDS, then the row of zeros after it.  With 16-byte aligned
-// parts of at most 8 x THREADS float4, each wave moves its 64-float4 chunks straight from
-// global memory into LDS (buffer_load_dwordx4 ... lds: lane i's 16 bytes land at the
-// chunk's LDS address + 16 i), all eight in flight, then waits for them.  One buffer
+// Part p of the table into LDS by THREADS threads, then the row of zeros after it.  With
+// 16-byte aligned parts of at most CHUNKS x THREADS float4, each wave moves its 64-float4
+// chunks straight from global memory into LDS (buffer_load_dwordx4 ... lds: lane i's 16
+// bytes land at the chunk's LDS address + 16 i), all CHUNKS in flight, then waits for
+// them.  One buffer
 // descriptor covers the part and the whole byte offset sits in the range-checked VGPR, so
 // the lanes of a chunk that runs past the part load zeros (into LDS inside the
 // 8 x THREADS float4, where the row of zeros goes anyway).  The chunk's LDS address and
 // its test against the part size are scalar.  Copied through registers instead, the loads
 // of a thread went out one at a time (the registers hold a tile's values), and the 64-bit
 // addresses of per-lane LDS-direct loads made the GEMV kernel spill.
-template <int V, int THREADS>
+template <int V, int THREADS, int CHUNKS = 8>
 __device__ __forceinline__ void copy_part(float *tab, bool vec, const float *C, int p,
                                           int64_t nfl, int64_t n4, int tid) {
     if (vec) {
@@ -156,9 +157,9 @@ __device__ __forceinline__ void copy_part(float *tab, bool vec, const float *C, 
             const_cast<float *>(C + static_cast<int64_t>(p) * nfl), 0,
             static_cast<int>(n4 * 16), 0x00020000);
         const int wb = __builtin_amdgcn_readfirstlane(tid & ~63);  // the wave's first thread
-        const int n4i = static_cast<int>(n4);  // at most 8 x THREADS
+        const int n4i = static_cast<int>(n4);  // at most CHUNKS x THREADS
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < CHUNKS; ++u) {
             const int base = u * THREADS + wb;  // float4 index of the wave's chunk
             if (base < n4i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -487,6 +488,14 @@ __device__ __forceinline__ int opaque(int v) {
     return v;
 }
 
+// Workgroup barrier with a fence on LDS only: the wave's LDS accesses complete before
+// it, but not its global stores (which __syncthreads() would wait for).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Stream words w_0 .. w_U of unit u (zeros past the range) and, if need_dst, the offset
 // in out of its SV values (-1 past the range).  Blocks are whole units, so a block's
 // words are its units' words: unit u's U words follow unit u - 1's (at u U), and its
@@ -531,10 +540,138 @@ __global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_c
     const int64_t n4 = nfl / 4;
     const bool vec = a.c_aligned && n4 <= 8 * THREADS;
 
-    const bool need_dst = !((S * V) % 4 == 0 && a.dense);  // the dense stores use none
     const uint32_t u_begin = blockIdx.x * a.units_per_wg;
     const uint32_t u_end = u_begin + a.units_per_wg < a.units ? u_begin + a.units_per_wg
                                                               : a.units;
+    // Dense output (ldo = N, 16-byte aligned): the units of a tile row are consecutive in
+    // out, so each row's values are restaged through LDS (the table part is done with by
+    // then) and stored as 1 KiB runs per wave.  A unit's float4 c sits in LDS slot
+    // j F4 + (c ^ swz(j)): 16 consecutive lanes then write, and read, 64 different banks.
+    // The two halves of the workgroup take different memory roles: the first copies the
+    // table parts into LDS, the second stores the decoded rows.  Vector memory operations
+    // of a wave complete in order, so a wave that both stored and copied would wait for
+    // its stores before each part it copies; here the stores drain while the next tile's
+    // parts arrive and its passes run.  Barriers fence LDS only (__syncthreads() would
+    // also wait for the global stores), and the stores go through a buffer descriptor that
+    // ends with the row's values, so every storing thread issues the same number of them
+    // and the tail is dropped by the range check.  The next tile's stream words are
+    // requested before this tile's stores, so waiting for them does not wait for the
+    // stores either.
+    constexpr bool kVec = (S * V) % 4 == 0;
+    if constexpr (kVec) {
+        if (a.dense) {
+            constexpr int F4 = (S * V) / 4;  // float4 per unit
+            constexpr uint32_t kTile = THREADS * RT;
+            constexpr int kHalf = THREADS / 2;  // threads of each role (whole waves)
+            const bool copier = tid < kHalf;
+            uint32_t wr[RT][NR];
+#pragma unroll
+            for (int i = 0; i < RT; ++i) {
+                uint32_t w[U + 1];
+                int64_t dst;
+                dec_unit_words<U, S * V>(a, u_begin + i * THREADS + tid, u_end, w, dst, false);
+                unit_regs<U>(wr[i], w);
+            }
+            if (copier) copy_part<V, kHalf, 16>(tab, vec, a.C, 0, nfl, n4, opaque(tid));
+            lds_barrier();
+            for (uint32_t t0 = u_begin; t0 < u_end; t0 += kTile) {
+                uint32_t val[RT][S][V];
+#pragma unroll
+                for (int i = 0; i < RT; ++i)
+#pragma unroll
+                    for (int q = 0; q < S; ++q)
+#pragma unroll
+                        for (int v = 0; v < V; ++v) val[i][q][v] = 0u;
+                for (int p = 0; p < a.parts; ++p) {
+                    uint32_t negbase = 0u - static_cast<uint32_t>(p) * dummy;
+                    asm volatile("" : "+s"(negbase));
+#pragma unroll
+                    for (int i = 0; i < RT; ++i)
+#pragma unroll
+                        for (int j = 0; j < NR; ++j) asm volatile("" : "+v"(wr[i][j]));
+#pragma unroll
+                    for (int i = 0; i < RT; ++i) {
+#pragma unroll
+                        for (int q0 = 0; q0 < S; q0 += Sh::B) {
+                            constexpr int B = Sh::B;
+                            float c[B][V];
+#pragma unroll
+                            for (int b = 0; b < B; ++b) {
+                                const uint32_t st = unit_state<KV>(wr[i], q0 + b, a.L);
+                                uint32_t off = (st << kLog) + negbase;
+                                off = off < dummy ? off : dummy;
+                                load_row<V>(c[b], reinterpret_cast<const char *>(tab) + off);
+                            }
+#pragma unroll
+                            for (int b = 0; b < B; ++b)
+#pragma unroll
+                                for (int v = 0; v < V; ++v)
+                                    val[i][q0 + b][v] |= __float_as_uint(c[b][v]);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                    if (p + 1 < a.parts) {
+                        lds_barrier();
+                        if (copier)
+                            copy_part<V, kHalf, 16>(tab, vec, a.C, p + 1, nfl, n4, opaque(tid));
+                        lds_barrier();
+                    }
+                }
+                // the next tile's stream words, requested before this tile's stores
+                const uint32_t next = t0 + kTile;
+                if (next < u_end) {
+#pragma unroll
+                    for (int i = 0; i < RT; ++i) {
+                        uint32_t w[U + 1];
+                        int64_t dst;
+                        dec_unit_words<U, S * V>(a, next + i * THREADS + tid, u_end, w, dst, false);
+                        unit_regs<U>(wr[i], w);
+                    }
+                }
+                float4 *st4 = reinterpret_cast<float4 *>(tab);
+#pragma unroll
+                for (int i = 0; i < RT; ++i) {
+                    lds_barrier();  // the table, or the previous row's values, are read
+                    const uint32_t swz_w = (static_cast<uint32_t>(tid) * F4 / 16) & (F4 - 1);
+#pragma unroll
+                    for (int f = 0; f < F4; ++f)
+                        st4[tid * F4 + (f ^ swz_w)] =
+                            make_float4(__uint_as_float(val[i][(4 * f) / V][(4 * f) % V]),
+                                        __uint_as_float(val[i][(4 * f + 1) / V][(4 * f + 1) % V]),
+                                        __uint_as_float(val[i][(4 * f + 2) / V][(4 * f + 2) % V]),
+                                        __uint_as_float(val[i][(4 * f + 3) / V][(4 * f + 3) % V]));
+                    lds_barrier();
+                    if (!copier) {
+                        const uint32_t r0 = t0 + i * THREADS;
+                        const uint32_t nun =
+                            r0 < u_end ? (u_end - r0 < THREADS ? u_end - r0 : THREADS) : 0u;
+                        const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+                            a.out + static_cast<int64_t>(r0) * (S * V), 0,
+                            static_cast<int>(nun * F4 * 16u), 0x00020000);
+                        const uint32_t ts = static_cast<uint32_t>(tid - kHalf);
+                        float4 o[2 * F4];
+#pragma unroll
+                        for (int f = 0; f < 2 * F4; ++f) {
+                            const uint32_t pidx = f * kHalf + ts;  // float4 of the row
+                            const uint32_t j = pidx / F4, c = pidx % F4;
+                            const uint32_t swz = (j * F4 / 16) & (F4 - 1);
+                            o[f] = st4[j * F4 + (c ^ swz)];
+                        }
+#pragma unroll
+                        for (int f = 0; f < 2 * F4; ++f)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, o[f]),
+                                ors, static_cast<int>((f * kHalf + ts) * 16u), 0, 0);
+                    }
+                }
+                lds_barrier();  // the last row's values are read
+                if (next < u_end && copier)
+                    copy_part<V, kHalf, 16>(tab, vec, a.C, 0, nfl, n4, opaque(tid));
+                lds_barrier();
+            }
+            return;
+        }
+    }
     for (uint32_t t0 = u_begin; t0 < u_end; t0 += THREADS * RT) {
         uint32_t wr[RT][NR];
         uint32_t val[RT][S][V];  // bit patterns of the decoded values
@@ -542,7 +679,7 @@ __global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_c
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
             uint32_t w[U + 1];
-            dec_unit_words<U, S * V>(a, t0 + i * THREADS + tid, u_end, w, dst[i], need_dst);
+            dec_unit_words<U, S * V>(a, t0 + i * THREADS + tid, u_end, w, dst[i], true);
             unit_regs<U>(wr[i], w);
 #pragma unroll
             for (int q = 0; q < S; ++q)
@@ -587,57 +724,22 @@ __global__ __launch_bounds__(THREADS, THREADS * kDecWgPerCu / 256) void decode_c
             }
         }
         constexpr bool kVec = (S * V) % 4 == 0;
-        constexpr int F4 = kVec ? (S * V) / 4 : 1;  // float4 per unit
-        if (kVec && a.dense) {
-            // The units of a tile row are consecutive in out: restage each row's values
-            // through LDS (the table part is done with) so that a wave stores 1 KiB runs.
-            // A unit's float4 c sits in LDS slot j F4 + (c ^ swz(j)): 16 consecutive lanes
-            // then write, and read, 64 different banks.
 #pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                const uint32_t r0 = t0 + i * THREADS;
-                __syncthreads();  // the table, or the previous row's values, are read
-                float4 *st4 = reinterpret_cast<float4 *>(tab);
-                const uint32_t swz_w = (static_cast<uint32_t>(tid) * F4 / 16) & (F4 - 1);
+        for (int i = 0; i < RT; ++i) {
+            float *o = a.out + dst[i];
+            if (dst[i] >= 0 && kVec && a.vec_out) {
 #pragma unroll
-                for (int f = 0; f < F4; ++f)
-                    st4[tid * F4 + (f ^ swz_w)] =
-                        make_float4(__uint_as_float(val[i][(4 * f) / V][(4 * f) % V]),
-                                    __uint_as_float(val[i][(4 * f + 1) / V][(4 * f + 1) % V]),
-                                    __uint_as_float(val[i][(4 * f + 2) / V][(4 * f + 2) % V]),
-                                    __uint_as_float(val[i][(4 * f + 3) / V][(4 * f + 3) % V]));
-                __syncthreads();
-                if (r0 < u_end) {
-                    const uint32_t nun = u_end - r0 < THREADS ? u_end - r0 : THREADS;
-                    float4 *o4 = reinterpret_cast<float4 *>(a.out + static_cast<int64_t>(r0) *
-                                                                        (S * V));
+                for (int f = 0; f < (kVec ? S * V : 0); f += 4)
+                    *reinterpret_cast<float4 *>(o + f) =
+                        make_float4(__uint_as_float(val[i][f / V][f % V]),
+                                    __uint_as_float(val[i][(f + 1) / V][(f + 1) % V]),
+                                    __uint_as_float(val[i][(f + 2) / V][(f + 2) % V]),
+                                    __uint_as_float(val[i][(f + 3) / V][(f + 3) % V]));
+            } else if (dst[i] >= 0) {
 #pragma unroll
-                    for (int f = 0; f < F4; ++f) {
-                        const uint32_t pidx = f * THREADS + tid;  // float4 of the row
-                        const uint32_t j = pidx / F4, c = pidx % F4;
-                        const uint32_t swz = (j * F4 / 16) & (F4 - 1);
-                        if (pidx < nun * F4) o4[pidx] = st4[j * F4 + (c ^ swz)];
-                    }
-                }
-            }
-        } else {
+                for (int q = 0; q < S; ++q)
 #pragma unroll
-            for (int i = 0; i < RT; ++i) {
-                float *o = a.out + dst[i];
-                if (dst[i] >= 0 && kVec && a.vec_out) {
-#pragma unroll
-                    for (int f = 0; f < (kVec ? S * V : 0); f += 4)
-                        *reinterpret_cast<float4 *>(o + f) =
-                            make_float4(__uint_as_float(val[i][f / V][f % V]),
-                                        __uint_as_float(val[i][(f + 1) / V][(f + 1) % V]),
-                                        __uint_as_float(val[i][(f + 2) / V][(f + 2) % V]),
-                                        __uint_as_float(val[i][(f + 3) / V][(f + 3) % V]));
-                } else if (dst[i] >= 0) {
-#pragma unroll
-                    for (int q = 0; q < S; ++q)
-#pragma unroll
-                        for (int v = 0; v < V; ++v) o[q * V + v] = __uint_as_float(val[i][q][v]);
-                }
+                    for (int v = 0; v < V; ++v) o[q * V + v] = __uint_as_float(val[i][q][v]);
             }
         }
     }
