@@ -34,7 +34,9 @@
  * Calls are asynchronous on `stream` (0 = the null stream); outputs are valid once the
  * stream has completed.  Argument checks happen on the host, synchronously, before
  * anything is enqueued; a call that returns an error has enqueued nothing.
- * The library keeps no state between calls apart from the per-thread error string.
+ * The library keeps no state between calls apart from the per-thread error string, a
+ * cache of per-kernel launch attributes and, for tcq_encode_noalloc only, its per-GPU
+ * scratch array (see there).
  */
 #ifndef TCQ_H
 #define TCQ_H
