@@ -5,7 +5,8 @@ are seeded random bitstreams with start states below 2^(L-kV) (every such stream
 of the trellis); nothing comes from the GPU encoder.  The cases cover the LDS-staged unit
 kernel for every (k*V, V) it is built for, with 1 to 8 codebook parts, several tiles per
 workgroup and a ragged last tile, both store widths (row strides with and without 16-byte
-alignment), and the per-block kernel that takes every other shape; the codebook carries
+alignment), codebooks that do not start on 16 bytes, and the per-block kernel that takes
+every other shape; the codebook carries
 -0.0, +0.0, a denormal and infinities, which must come out unchanged.
 """
 import sys
@@ -46,11 +47,16 @@ def _codebook(oracle_lib, L, V, seed):
     return C
 
 
-def _gpu_decode(bits, s0, C, M, N, L, k, V, T, ldo=None):
+def _gpu_decode(bits, s0, C, M, N, L, k, V, T, ldo=None, c_shift=0):
+    """c_shift > 0 places the codebook c_shift floats into its allocation (not 16-byte
+    aligned for c_shift = 1, 2, 3)."""
     ldo = N if ldo is None else ldo
     bt = torch.from_numpy(bits.view(np.int32)).cuda()
     st = torch.from_numpy(s0.view(np.int32)).cuda()
-    Ct = torch.from_numpy(np.ascontiguousarray(C)).cuda()
+    flat = torch.from_numpy(np.ascontiguousarray(C).reshape(-1))
+    Cbuf = torch.full((flat.numel() + c_shift,), float("nan"), dtype=torch.float32)
+    Cbuf[c_shift:] = flat
+    Ct = Cbuf.cuda()[c_shift:]
     out = torch.full((max(M, 1), ldo), float("nan"), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
     _lib.tcq_decode(bt.data_ptr(), st.data_ptr(), Ct.data_ptr(), M, N, L, k, V, T,
@@ -93,6 +99,26 @@ def test_decode_bitwise(oracle_lib, L, k, V, T, M, N, ldo):
     bits, s0 = _streams(rng, M * (N // T), L, k, V, T)
     ref = oracle_lib.decode_matrix(bits, s0, C, M, N, L, k, V, T)
     out = _gpu_decode(bits, s0, C, M, N, L, k, V, T, ldo)
+    assert np.array_equal(out[:, :N].view(np.uint32), ref.view(np.uint32))
+    if ldo is not None and ldo > N:
+        assert np.all(np.isnan(out[:, N:])), "decode wrote past N"
+
+
+@pytest.mark.parametrize("L,k,V,T,M,N,ldo,c_shift", [
+    (16, 2, 1, 256, 64, 2048, None, 1),   # dense rows, two parts
+    (16, 2, 2, 256, 40, 1024, None, 2),   # dense rows, four parts
+    (16, 3, 1, 256, 24, 1536, None, 3),   # dense rows, three-word units
+    (16, 2, 1, 256, 33, 1024, 1027, 1),   # strided rows
+    (7, 1, 2, 64, 5, 256, None, 1),       # one part smaller than the workgroup
+])
+def test_decode_unaligned_codebook(oracle_lib, L, k, V, T, M, N, ldo, c_shift):
+    """A codebook that does not start on 16 bytes is copied into LDS float by float."""
+    _say(f"decode L={L} k={k} V={V} T={T} M={M} N={N} ldo={ldo} codebook +{c_shift} floats")
+    rng = np.random.default_rng(L * 1000 + k * 100 + V * 10 + M + 7 * c_shift)
+    C = _codebook(oracle_lib, L, V, 77 + L)
+    bits, s0 = _streams(rng, M * (N // T), L, k, V, T)
+    ref = oracle_lib.decode_matrix(bits, s0, C, M, N, L, k, V, T)
+    out = _gpu_decode(bits, s0, C, M, N, L, k, V, T, ldo, c_shift)
     assert np.array_equal(out[:, :N].view(np.uint32), ref.view(np.uint32))
     if ldo is not None and ldo > N:
         assert np.all(np.isnan(out[:, N:])), "decode wrote past N"

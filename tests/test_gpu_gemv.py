@@ -39,10 +39,14 @@ def _random_streams(rng, nb, L, k, V, T):
     return bits, s0
 
 
-def _gpu_gemv(bits, s0, C, x, M, N, L, k, V, T):
+def _gpu_gemv(bits, s0, C, x, M, N, L, k, V, T, c_shift=0):
+    """c_shift > 0 places the codebook c_shift floats into its allocation."""
     bt = torch.from_numpy(bits.view(np.int32)).cuda()
     st = torch.from_numpy(s0.view(np.int32)).cuda()
-    Ct = torch.from_numpy(np.ascontiguousarray(C)).cuda()
+    flat = torch.from_numpy(np.ascontiguousarray(C).reshape(-1))
+    Cbuf = torch.full((flat.numel() + c_shift,), float("nan"), dtype=torch.float32)
+    Cbuf[c_shift:] = flat
+    Ct = Cbuf.cuda()[c_shift:]
     xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
     y = api.decode_gemv(bt, st, Ct, xt, M, N, L, k, V, T)
     torch.cuda.synchronize()
@@ -115,6 +119,25 @@ def test_gemv_full_size_sampled_rows(oracle_lib, M, N, L, k, V, T):
     sel = (rows[:, None] * per_row + np.arange(per_row)[None, :]).reshape(-1)
     yref, What = oracle.decode_gemv(bits[sel], s0[sel], C, x, rows.size, N, L, k, V, T)
     _check(y[rows], yref, What, x, M, N, L, k, V, T)
+
+
+@pytest.mark.parametrize("L,k,V,T,M,N,c_shift", [(16, 2, 1, 256, 7, 2048 + 256, 1),
+                                                   (16, 2, 2, 256, 4, 768, 3),
+                                                   (16, 3, 1, 256, 5, 1024, 2)])
+def test_gemv_unaligned_codebook(oracle_lib, L, k, V, T, M, N, c_shift):
+    """A codebook that does not start on 16 bytes is copied into LDS float by float; the
+    result must equal the aligned launch's bit for bit."""
+    import oracle
+    _say(f"gemv L={L} k={k} V={V} T={T} M={M} N={N} codebook +{c_shift} floats")
+    rng = np.random.default_rng(L * 1000 + k * 100 + V * 10 + T + c_shift)
+    C = oracle.make_codebook(L, V, 50 + L)
+    bits, s0 = _random_streams(rng, M * (N // T), L, k, V, T)
+    x = rng.standard_normal(N).astype(np.float32)
+    yref, What = oracle.decode_gemv(bits, s0, C, x, M, N, L, k, V, T)
+    y = _gpu_gemv(bits, s0, C, x, M, N, L, k, V, T, c_shift)
+    _check(y, yref, What, x, M, N, L, k, V, T)
+    y0 = _gpu_gemv(bits, s0, C, x, M, N, L, k, V, T)
+    assert np.array_equal(y.view(np.uint32), y0.view(np.uint32))
 
 
 def test_gemv_empty_and_deterministic(oracle_lib):
