@@ -244,10 +244,10 @@ int tcq_encode_ldlq(const float *W, int64_t M, int64_t N, int64_t ldw, const flo
                     size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Soft trellis (BCJR) at temperature tau.  BCJR-QAT abstract on the aqora listing: the
- * Viterbi argmax is replaced by the BCJR forward-backward sum-product at a temperature;
- * the soft codeword is the Boltzmann expectation of the emitted values over all paths,
- * and the hard (Viterbi) code comes back as the temperature goes to 0.
+ * Soft trellis (BCJR) at temperature tau.  BCJR-QAT abstract on the aqora listing: a
+ * tempered forward-backward pass stands in for the hard minimum of the Viterbi search;
+ * each output is the mean emitted value when paths are weighted by exp(-J / tau), and
+ * as tau falls to 0 the output returns to the hard (Viterbi) reconstruction.
  *
  * Every path of a block (free start, as tcq_encode) has energy J, the same weighted
  * squared error tcq_encode minimises, and probability exp(-J / tau) / Z.

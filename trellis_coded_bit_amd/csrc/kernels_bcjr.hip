@@ -1,7 +1,7 @@
-// Soft trellis (BCJR) at temperature tau.  BCJR-QAT abstract (aqora listing): the
-// Viterbi argmax is replaced by the BCJR forward-backward sum-product at a temperature;
-// the soft codeword is the Boltzmann expectation of the emitted values over all trellis
-// paths, and the hard code comes back as the temperature goes to 0.
+// Soft trellis (BCJR) at temperature tau.  BCJR-QAT abstract (aqora listing): a tempered
+// forward-backward pass stands in for the hard minimum of the Viterbi search; each output
+// is the mean emitted value when paths are weighted by exp(-J/tau), and as tau falls to 0
+// the output returns to the Viterbi reconstruction.
 //
 // Energy of a path = the weighted squared error the Viterbi search minimises; probability
 // of a path = exp(-J/tau) / Z.  Work is in base-2 logs: the log-weight of state s at a

@@ -33,11 +33,12 @@ struct CtxL : Ctx {
     BpBuf bpb;
 };
 
-// Groups of codebook in flight.  Measured on MI355X: at d = 1 a 12-deep ring beats a
-// 16-deep one (41.7 against 42.0 ms at 2048 x 2048); the weighted search, with one more
-// multiply per update between the loads, gains 0.6 % from the deeper ring.
+// Groups of codebook in flight.  Measured on MI355X with the transposition rounds spread
+// over the segments: 12 deep for both searches (a 16-deep ring leaves the weighted
+// kernel short of registers, and it spills in the loop: 193.5 against 172.1 ms at
+// 4096 x 4096; at d = 1 16 deep gains nothing).
 template <bool WEIGHTED>
-constexpr int kRing = WEIGHTED ? 16 : 12;
+constexpr int kRing = 12;
 
 __global__ __launch_bounds__(256) void l16_prepare_kernel(const float *__restrict__ C,
                                                           float4 *__restrict__ out) {
@@ -138,24 +139,6 @@ __device__ __forceinline__ void acs_segment_impl(uint32_t (&J)[kRegs],
     bpb.store(bp_word, acc);
 }
 
-// Groups I0 .. I0 + 7 of segment SEG, their backpointer bits shifted into acc (the word
-// is stored by the caller once all 16 groups are in).
-template <int SEG, bool WEIGHTED, int NM, int I0, int... I>
-__device__ __forceinline__ void acs_half_impl(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
-                                              __amdgpu_buffer_rsrc_t rs, uint32_t voff, float wt,
-                                              float dt, uint32_t &acc,
-                                              std::integer_sequence<int, I...>) {
-    (acs_group<SEG, WEIGHTED, NM, I0 + I>(J, ring, rs, voff, wt, dt, acc), ...);
-}
-
-template <int SEG, bool WEIGHTED, int NM, int I0>
-__device__ __forceinline__ void acs_half(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
-                                         const CtxL &cx, const StepIn &in, uint32_t &acc) {
-    constexpr int P = seg_step(SEG);
-    acs_half_impl<SEG, WEIGHTED, NM, I0>(J, ring, cx.rs, cx.voff, in.w[P - 1], in.d[P - 1],
-                                         acc, std::make_integer_sequence<int, 8>{});
-}
-
 template <int SEG, bool WEIGHTED, int NM>
 __device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                             const CtxL &cx, int t0, const StepIn &in) {
@@ -166,6 +149,29 @@ __device__ __forceinline__ void acs_segment(uint32_t (&J)[kRegs], float4 (&ring)
                                         std::make_integer_sequence<int, 16>{});
 }
 
+template <int SEG, bool WEIGHTED, int NM, class X, int... I>
+__device__ __forceinline__ void acs_segment_x_impl(uint32_t (&J)[kRegs],
+                                                   float4 (&ring)[kRing<WEIGHTED>],
+                                                   const CtxL &cx, float wt, float dt,
+                                                   int bp_word, const X &x,
+                                                   std::integer_sequence<int, I...>) {
+    uint32_t acc = 0;
+    ((acs_group<SEG, WEIGHTED, NM, I>(J, ring, cx.rs, cx.voff, wt, dt, acc),
+      x.template step<I>(J, cx)),
+     ...);
+    cx.bpb.store(bp_word, acc);
+}
+// acs_segment with LDS work X interleaved.
+template <int SEG, bool WEIGHTED, int NM, class X>
+__device__ __forceinline__ void acs_segment_x(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
+                                              const CtxL &cx, int t0, const StepIn &in,
+                                              const X &x) {
+    constexpr int P = seg_step(SEG);
+    const int t = t0 + P - 1;
+    acs_segment_x_impl<SEG, WEIGHTED, NM>(J, ring, cx, in.w[P - 1], in.d[P - 1],
+                                          2 * kThreads * t + seg_half(SEG), x,
+                                          std::make_integer_sequence<int, 16>{});
+}
 // Segment 2 (step 1 of the odd groups) with round 1 of the transposition read into the
 // registers it consumes: the four values of group i + kReadAhead are requested before
 // group i is computed, so at most 4 * (kReadAhead + 1) reads are in flight (the LDS
@@ -188,42 +194,44 @@ __device__ __forceinline__ void seg2_reading(uint32_t (&J)[kRegs], float4 (&ring
 }
 
 // Super-step (steps t0+1 .. t0+3) under naming NM, with the weights (and d) of its three
-// steps in `in`; those of the next super-step are requested into `next`.  On entry
-// round 1 of the previous transposition is still in LDS (the even registers already
-// hold round 0); on exit the costs have been transposed again for naming 1 - NM, with
-// round 1 left in LDS.
+// steps in `in`; those of the next super-step are requested into `next`.  On entry the
+// even registers hold round 0 of the previous transposition, and round 1 of it is still
+// in the registers of naming 1 - NM with r[6] = 1 (the odd groups of this naming, which
+// segments 0 and 1 do not touch): segments 0 and 1 write it to LDS as they go, segment 2
+// reads it back group by group.  Segment 4 (step 3 of the r[6] = 0 half) writes round 0
+// of this super-step's transposition as its groups finish, and segment 5 (the r[6] = 1
+// half) reads it back into the same registers.  On exit round 1 is left in registers
+// for the next super-step (or the tail) to write.
 template <bool WEIGHTED, int NM>
 __device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                            const CtxL &cx, int t0, const StepIn &in,
                                            StepIn &next) {
-    acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
-    acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0, in);
+    acs_segment_x<0, WEIGHTED, NM>(J, ring, cx, t0, in, WriteLds<1 - NM, 1, 2, 0>{});
+    acs_segment_x<1, WEIGHTED, NM>(J, ring, cx, t0, in, WriteLds<1 - NM, 1, 2, 32>{});
     __syncthreads();  // round-1 values written by every wave
     seg2_reading<WEIGHTED, NM>(J, ring, cx, t0, in, std::make_integer_sequence<int, 16>{});
     acs_segment<3, WEIGHTED, NM>(J, ring, cx, t0, in);
-    acs_segment<4, WEIGHTED, NM>(J, ring, cx, t0, in);
     __syncthreads();  // every wave has read round 1
-    round_write<NM, 0>(J, cx);
-    // segment 5 works on the r[6] = 1 registers only, so its second half runs while the
-    // round-0 values (which refill the r[6] = 0 registers) are on their way in
-    uint32_t acc5 = 0;
-    acs_half<5, WEIGHTED, NM, 0>(J, ring, cx, in, acc5);
+    acs_segment_x<4, WEIGHTED, NM>(J, ring, cx, t0, in, WriteRound0Lagged<NM, 4>{});
+    round_write_range<NM, 0, 60, 4>(J, cx);
     next = load_steps<WEIGHTED>(cx, t0 + 3);  // complete by the barrier below
     __syncthreads();  // round-0 values written by every wave
-    round_read<NM, 0>(J, cx);
-    acs_half<5, WEIGHTED, NM, 8>(J, ring, cx, in, acc5);
-    cx.bpb.store(2 * kThreads * (t0 + 2) + seg_half(5), acc5);
+    acs_segment_x<5, WEIGHTED, NM>(J, ring, cx, t0, in, ReadLds<NM, 0, 1>{});
     __syncthreads();  // every wave has read round 0
-    round_write<NM, 1>(J, cx);
 }
 
 // The last R = 1 or 2 steps (segments 0..3 in order; for one step the ring is refilled
-// where the order departs from a full super-step).
+// where the order departs from a full super-step), under naming NM.  Round 1 of the last
+// transposition (naming 1 - NM) is written while segments 0 (and 1) run.
 template <bool WEIGHTED, int NM, int R>
 __device__ __forceinline__ void tail_steps(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                            const CtxL &cx, int t0, const StepIn &in) {
-    acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
-    if constexpr (R == 2) acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0, in);
+    if constexpr (R == 2) {
+        acs_segment_x<0, WEIGHTED, NM>(J, ring, cx, t0, in, WriteLds<1 - NM, 1, 2, 0>{});
+        acs_segment_x<1, WEIGHTED, NM>(J, ring, cx, t0, in, WriteLds<1 - NM, 1, 2, 32>{});
+    } else {
+        acs_segment_x<0, WEIGHTED, NM>(J, ring, cx, t0, in, WriteLds<1 - NM, 1, 4, 0>{});
+    }
     __syncthreads();
     round_read<1 - NM, 1>(J, cx);
     if constexpr (R == 1) ring_fill<32>(ring, cx.rs, cx.voff);
@@ -271,13 +279,13 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     float4 ring[kRing<WEIGHTED>];
     ring_fill<0>(ring, cx.rs, cx.voff);
 
-    // Every super-step ends with a transposition whose second round is read at the start
-    // of the next one; the all-zero start is staged the same way, so all super-steps run
-    // the same branch-free code.  Super-steps alternate between namings 1 and 0 so that
-    // the last one runs under naming 1 and the tail under naming 0.
+    // Every super-step ends with a transposition whose second round is written and read
+    // during the next one; the all-zero start is staged the same way (whatever registers
+    // the first super-step writes out hold zeros), so all super-steps run the same
+    // branch-free code.  Super-steps alternate between namings 1 and 0 so that the last
+    // one runs under naming 1 and the tail under naming 0.
 #pragma unroll
     for (int r = 0; r < kRegs; ++r) asm volatile("" : "+v"(J[r]));  // keep the zeros opaque
-    round_write<1, 1>(J, cx);
     const int Q = n / 3;
     const int R = n % 3;
     StepIn in = load_steps<WEIGHTED>(cx, 0);
@@ -297,7 +305,8 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     } else if (R == 2) {
         tail_steps<WEIGHTED, 0, 2>(J, ring, cx, 3 * Q, in);
     } else {
-        __syncthreads();  // collect the last round
+        round_write<1, 1>(J, cx);  // the last round (zeros if there was no super-step)
+        __syncthreads();
         round_read<1, 1>(J, cx);
     }
 

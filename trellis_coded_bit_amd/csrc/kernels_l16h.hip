@@ -226,6 +226,28 @@ __device__ __forceinline__ void acsh_group(uint32_t (&J)[kRegs], float4 (&ring)[
         acsh_group_plain<SEG, NM, I>(J, acc);
 }
 
+// Segment SEG with LDS work X issued after each group (l16_device.h).
+template <int SEG, bool WEIGHTED, int NM, int V, int MP, class X, int... I>
+__device__ __forceinline__ void acsh_segment_x_impl(uint32_t (&J)[kRegs],
+                                                    float4 (&ring)[Ring<V>::kSize],
+                                                    const CtxH &cx, const StepInH &in,
+                                                    int bp_word, const X &x,
+                                                    std::integer_sequence<int, I...>) {
+    uint32_t acc = 0;
+    ((acsh_group<SEG, WEIGHTED, NM, V, MP, I>(J, ring, cx, in, acc), x.template step<I>(J, cx)),
+     ...);
+    cx.bpb.store(bp_word, acc);
+}
+template <int SEG, bool WEIGHTED, int NM, int V, int MP, class X>
+__device__ __forceinline__ void acsh_segment_x(uint32_t (&J)[kRegs],
+                                               float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
+                                               int h0, const StepInH &in, const X &x) {
+    constexpr int P = seg_step(SEG);
+    const int h = h0 + P - 1;
+    acsh_segment_x_impl<SEG, WEIGHTED, NM, V, MP>(J, ring, cx, in, 2 * kThreads * h + seg_half(SEG),
+                                                  x, std::make_integer_sequence<int, 16>{});
+}
+
 // Segment 2 (step 1 of the odd groups) with round 1 of the transposition read into the
 // registers it consumes, the four values of group i + 3 requested before group i (at
 // most 16 reads in flight; the LDS wait counter counts at most 15).
@@ -247,44 +269,28 @@ __device__ __forceinline__ void seg2_reading_h(uint32_t (&J)[kRegs],
     cx.bpb.store(2 * kThreads * h0 + seg_half(2), acc);
 }
 
-// Groups I0 .. I0 + 7 of segment 5, their backpointer bits shifted into acc.
-template <bool WEIGHTED, int NM, int V, int MP, int I0, int... I>
-__device__ __forceinline__ void seg5_half_h(uint32_t (&J)[kRegs],
-                                            float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
-                                            const StepInH &in, uint32_t &acc,
-                                            std::integer_sequence<int, I...>) {
-    (acsh_group<5, WEIGHTED, NM, V, MP, I0 + I>(J, ring, cx, in, acc), ...);
-}
-
 // Super-step under naming NM and pattern MP, with the weights of its half-steps in `in`
-// and those of the next super-step requested into `next`; entry and exit as in
-// kernels_l16.hip.
+// and those of the next super-step requested into `next`; the transposition rounds are
+// spread over the segments as in kernels_l16.hip (round 1 of the previous transposition
+// written by segments 0 and 1 and read by segment 2, round 0 written behind segment 4
+// and read by segment 5, round 1 left in registers for the next super-step or the tail).
 template <bool WEIGHTED, int NM, int V, int MP>
 __device__ __forceinline__ void super_step_h(uint32_t (&J)[kRegs],
                                              float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
                                              int h0, const StepInH &in, StepInH &next) {
-    acsh_segment<0, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in);
-    acsh_segment<1, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in);
+    acsh_segment_x<0, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in, WriteLds<1 - NM, 1, 2, 0>{});
+    acsh_segment_x<1, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in, WriteLds<1 - NM, 1, 2, 32>{});
     __syncthreads();  // round-1 values written by every wave
     seg2_reading_h<WEIGHTED, NM, V, MP>(J, ring, cx, h0, in,
                                         std::make_integer_sequence<int, 16>{});
     acsh_segment<3, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in);
-    acsh_segment<4, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in);
     __syncthreads();  // every wave has read round 1
-    round_write<NM, 0>(J, cx);
-    // segment 5 works on the r[6] = 1 registers only, so its second half runs while the
-    // round-0 values (which refill the r[6] = 0 registers) are on their way in
-    uint32_t acc5 = 0;
-    seg5_half_h<WEIGHTED, NM, V, MP, 0>(J, ring, cx, in, acc5,
-                                        std::make_integer_sequence<int, 8>{});
+    acsh_segment_x<4, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in, WriteRound0Lagged<NM, 4>{});
+    round_write_range<NM, 0, 60, 4>(J, cx);
     next = load_h<WEIGHTED, V>(cx, h0 + 3);
     __syncthreads();  // round-0 values written by every wave
-    round_read<NM, 0>(J, cx);
-    seg5_half_h<WEIGHTED, NM, V, MP, 8>(J, ring, cx, in, acc5,
-                                        std::make_integer_sequence<int, 8>{});
-    cx.bpb.store(2 * kThreads * (h0 + 2) + seg_half(5), acc5);
+    acsh_segment_x<5, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in, ReadLds<NM, 0, 1>{});
     __syncthreads();  // every wave has read round 0
-    round_write<NM, 1>(J, cx);
 }
 
 // The last R = 1 or 2 half-steps (segments 0..3 in order) under naming 0.  The metric
@@ -293,8 +299,12 @@ __device__ __forceinline__ void super_step_h(uint32_t (&J)[kRegs],
 template <bool WEIGHTED, int V, int MP, int R>
 __device__ __forceinline__ void tail_h(uint32_t (&J)[kRegs], float4 (&ring)[Ring<V>::kSize],
                                        const CtxH &cx, int h0, const StepInH &in) {
-    acsh_segment<0, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
-    if constexpr (R == 2) acsh_segment<1, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
+    if constexpr (R == 2) {
+        acsh_segment_x<0, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in, WriteLds<1, 1, 2, 0>{});
+        acsh_segment_x<1, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in, WriteLds<1, 1, 2, 32>{});
+    } else {
+        acsh_segment_x<0, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in, WriteLds<1, 1, 4, 0>{});
+    }
     __syncthreads();
     round_read<1, 1>(J, cx);
     acsh_segment<2, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
@@ -343,7 +353,8 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
     constexpr int RS = Ring<V>::kSize;
     float4 ring[RS];
     ringh_prime<V, 0, 0>(ring, cx.rs, cx.voff, std::make_integer_sequence<int, RS>{});
-    round_write<1, 1>(J, cx);
+    // the all-zero start is round 1 of a transposition that the first super-step (or the
+    // tail) writes out as it goes
 
     const int nh = 2 * n;
     const int Q = nh / 3;
@@ -375,6 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
         if (Q & 1) tail_h<WEIGHTED, V, 1, 2>(J, ring, cx, 3 * Q, in);
         else tail_h<WEIGHTED, V, 0, 2>(J, ring, cx, 3 * Q, in);
     } else {
+        round_write<1, 1>(J, cx);
         __syncthreads();
         round_read<1, 1>(J, cx);
     }

@@ -149,6 +149,29 @@ __device__ __forceinline__ void acs3_segment_impl(uint32_t (&J)[kRegs],
     *bp_word = acc;
 }
 
+// acs3_segment with LDS work X issued after each group (l16_device.h).
+template <int SEG, bool WEIGHTED, int NM, class X, int... I>
+__device__ __forceinline__ void acs3_segment_x_impl(uint32_t (&J)[kRegs],
+                                                    float4 (&ring)[kPrefetch3], const Ctx &cx,
+                                                    float wt, float dt, uint32_t *bp_word,
+                                                    const X &x, std::integer_sequence<int, I...>) {
+    uint32_t acc = 0;
+    ((acs3_group<SEG, WEIGHTED, NM, I>(J, ring, cx.rs, cx.voff, wt, dt, acc),
+      x.template step<I>(J, cx)),
+     ...);
+    *bp_word = acc;
+}
+template <int SEG, bool WEIGHTED, int NM, class X>
+__device__ __forceinline__ void acs3_segment_x(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch3],
+                                               const Ctx &cx, int t0, const StepIn &in,
+                                               const X &x) {
+    constexpr int P = seg3_step(SEG);
+    const int t = t0 + P - 1;
+    acs3_segment_x_impl<SEG, WEIGHTED, NM>(J, ring, cx, in.w[P - 1], in.d[P - 1],
+                                           cx.bp + 2 * kThreads * t + seg3_half(SEG), x,
+                                           std::make_integer_sequence<int, 8>{});
+}
+
 template <int SEG, bool WEIGHTED, int NM>
 __device__ __forceinline__ void acs3_segment(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch3],
                                              const Ctx &cx, int t0, const StepIn &in) {
@@ -193,39 +216,28 @@ __device__ __forceinline__ void seg1_reading3(uint32_t (&J)[kRegs], float4 (&rin
     cx.bp[2 * kThreads * t0 + seg3_half(1)] = acc;
 }
 
-// Groups I0 .. I0 + 3 of segment 3, their backpointer bits shifted into acc.
-template <bool WEIGHTED, int NM, int I0, int... I>
-__device__ __forceinline__ void seg3_quarter(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch3],
-                                             const Ctx &cx, const StepIn &in, uint32_t &acc,
-                                             std::integer_sequence<int, I...>) {
-    (acs3_group<3, WEIGHTED, NM, I0 + I>(J, ring, cx.rs, cx.voff, in.w[1], in.d[1], acc), ...);
-}
-
 // Super-step (steps t0+1, t0+2) under naming NM, with the weights (and d) of its two
 // steps in `in`; those of the next super-step are requested into `next` and complete at
 // a barrier (a wait for a scalar load would also wait for every LDS operation in flight).
-// Entry and exit as in kernels_l16.hip.
+// The transposition rounds are spread over the segments as in kernels_l16.hip: segment 0
+// (even step-1 groups) writes round 1 of the previous transposition, which is still in
+// the odd groups' registers; segment 1 reads it back; segment 2 (step 2, the r[6] = 0
+// half) writes round 0 as its groups finish and segment 3 (the r[6] = 1 half) reads it
+// back.  Round 1 is left in registers for the next super-step (or the tail).
 template <bool WEIGHTED, int NM>
 __device__ __forceinline__ void super_step3(uint32_t (&J)[kRegs], float4 (&ring)[kPrefetch3],
                                             const Ctx &cx, int t0, const StepIn &in,
                                             StepIn &next) {
-    acs3_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
+    acs3_segment_x<0, WEIGHTED, NM>(J, ring, cx, t0, in, WriteLds<1 - NM, 1, 8, 0>{});
     __syncthreads();  // round-1 values written by every wave
     seg1_reading3<WEIGHTED, NM>(J, ring, cx, t0, in, std::make_integer_sequence<int, 8>{});
-    acs3_segment<2, WEIGHTED, NM>(J, ring, cx, t0, in);
     __syncthreads();  // every wave has read round 1
-    round_write<NM, 0>(J, cx);
-    // segment 3 works on the r[6] = 1 registers only, so its second half runs while the
-    // round-0 values (which refill the r[6] = 0 registers) are on their way in
-    uint32_t acc3 = 0;
-    seg3_quarter<WEIGHTED, NM, 0>(J, ring, cx, in, acc3, std::make_integer_sequence<int, 4>{});
+    acs3_segment_x<2, WEIGHTED, NM>(J, ring, cx, t0, in, WriteRound0Lagged<NM, 8>{});
+    round_write_range<NM, 0, 56, 8>(J, cx);
     next = load_steps<WEIGHTED>(cx, t0 + 2);
     __syncthreads();  // round-0 values written by every wave
-    round_read<NM, 0>(J, cx);
-    seg3_quarter<WEIGHTED, NM, 4>(J, ring, cx, in, acc3, std::make_integer_sequence<int, 4>{});
-    cx.bp[2 * kThreads * (t0 + 1) + seg3_half(3)] = acc3;
+    acs3_segment_x<3, WEIGHTED, NM>(J, ring, cx, t0, in, ReadLds<NM, 0, 2>{});
     __syncthreads();  // every wave has read round 0
-    round_write<NM, 1>(J, cx);
 }
 
 template <int P, int NM>
@@ -265,7 +277,8 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16k3_kernel(
     for (int r = 0; r < kRegs; ++r) asm volatile("" : "+v"(J[r]));
     float4 ring[kPrefetch3];
     ring3_fill<0>(ring, cx.rs, cx.voff);
-    round_write<1, 1>(J, cx);
+    // the all-zero start is round 1 of a transposition that the first super-step (or the
+    // tail) writes out as it goes
 
     const int Q = n / 2;
     const int R = n % 2;
@@ -282,11 +295,12 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16k3_kernel(
         in = next;
     }
     if (R == 1) {  // one more step: segments 0 and 1 under naming 0
-        acs3_segment<0, WEIGHTED, 0>(J, ring, cx, 2 * Q, in);
+        acs3_segment_x<0, WEIGHTED, 0>(J, ring, cx, 2 * Q, in, WriteLds<1, 1, 8, 0>{});
         __syncthreads();
         round_read<1, 1>(J, cx);
         acs3_segment<1, WEIGHTED, 0>(J, ring, cx, 2 * Q, in);
     } else {
+        round_write<1, 1>(J, cx);
         __syncthreads();
         round_read<1, 1>(J, cx);
     }

@@ -157,6 +157,17 @@ __device__ __forceinline__ void round_write(const uint32_t (&J)[kRegs], const Ct
         lds_put(cx.wb[bit(r, 4)], off - bit(r, 4) * 4u * 2112u * 8u, J[phys(NM, r)]);
     }
 }
+// Registers I0 .. I0 + CNT - 1 of round RHO (the part of round_write a segment issues
+// between its groups).
+template <int NM, int RHO, int I0, int CNT>
+__device__ __forceinline__ void round_write_range(const uint32_t (&J)[kRegs], const Ctx &cx) {
+#pragma unroll
+    for (int i = I0; i < I0 + CNT; ++i) {
+        const uint32_t r = 64u * RHO + i;
+        const uint32_t off = 4u * lds_write_reg(r);
+        lds_put(cx.wb[bit(r, 4)], off - bit(r, 4) * 4u * 2112u * 8u, J[phys(NM, r)]);
+    }
+}
 // The four registers of group g = 2 i + RHO at step 1 (the registers the next segment
 // that needs round RHO consumes together).
 template <int NM, int RHO, int I>
@@ -175,11 +186,54 @@ __device__ __forceinline__ void round_read_groups(uint32_t (&J)[kRegs], const Ct
                                                   std::integer_sequence<int, I...>) {
     (round_read_group<NM, RHO, I>(J, cx), ...);
 }
+// std::integer_sequence<int, K + I...>
+template <int K, int... I>
+__device__ __forceinline__ constexpr std::integer_sequence<int, (K + I)...> shifted_seq(
+    std::integer_sequence<int, I...>) {
+    return {};
+}
 // All 64 registers r[0] = RHO, group by group.
 template <int NM, int RHO>
 __device__ __forceinline__ void round_read(uint32_t (&J)[kRegs], const Ctx &cx) {
     round_read_groups<NM, RHO>(J, cx, std::make_integer_sequence<int, 16>{});
 }
+
+// LDS work spread over the groups of a segment, so that a transposition round drains
+// while the VALU computes instead of in one burst behind a barrier (every wave reaches
+// the burst at the same time, and a wave issues nothing else until its LDS queue has
+// taken the whole burst).  After group I of the segment, `step<I>` issues its share.
+struct NoLds {
+    template <int I>
+    __device__ __forceinline__ void step(uint32_t (&)[kRegs], const Ctx &) const {}
+};
+// Round RHO of naming NM written PER registers per group, from register I0 + PER * I of
+// the round (pairs of consecutive registers share one ds_write2).
+template <int NM, int RHO, int PER, int I0>
+struct WriteLds {
+    template <int I>
+    __device__ __forceinline__ void step(uint32_t (&J)[kRegs], const Ctx &cx) const {
+        round_write_range<NM, RHO, I0 + PER * I, PER>(J, cx);
+    }
+};
+// Round 0 of naming NM written behind the segment of the super-step's last step that
+// covers the r[6] = 0 half, whose group I holds registers GS * I .. GS * I + GS - 1
+// (GS = 4 for 2-bit steps, 8 for 3-bit steps): after group I the registers of group
+// I - 1, whose costs are final; the caller writes the last group's after the segment.
+template <int NM, int GS>
+struct WriteRound0Lagged {
+    template <int I>
+    __device__ __forceinline__ void step(uint32_t (&J)[kRegs], const Ctx &cx) const {
+        if constexpr (I >= 1) round_write_range<NM, 0, GS * (I - 1), GS>(J, cx);
+    }
+};
+// Round RHO read into naming 1 - NM, PER of its 16 register groups per group.
+template <int NM, int RHO, int PER>
+struct ReadLds {
+    template <int I>
+    __device__ __forceinline__ void step(uint32_t (&J)[kRegs], const Ctx &cx) const {
+        round_read_groups<NM, RHO>(J, cx, shifted_seq<PER * I>(std::make_integer_sequence<int, PER>{}));
+    }
+};
 
 // Lowest-index minimum over the workgroup: (bv, bi) are each lane's best cost pattern
 // and state; lane 0 of wave 0 writes the chosen end state and its cost.
