@@ -222,16 +222,15 @@ __device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[
 
 // The last R = 1 or 2 steps (segments 0..3 in order; for one step the ring is refilled
 // where the order departs from a full super-step), under naming NM.  Round 1 of the last
-// transposition (naming 1 - NM) is written while segments 0 (and 1) run.
+// transposition (naming 1 - NM) is written first, in one go: spread over the tail's
+// segments it left the compiler short of registers there (spills to scratch, once per
+// block, about 2 GB of extra HBM traffic per launch at 2048 x 2048).
 template <bool WEIGHTED, int NM, int R>
 __device__ __forceinline__ void tail_steps(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                            const CtxL &cx, int t0, const StepIn &in) {
-    if constexpr (R == 2) {
-        acs_segment_x<0, WEIGHTED, NM>(J, ring, cx, t0, in, WriteLds<1 - NM, 1, 2, 0>{});
-        acs_segment_x<1, WEIGHTED, NM>(J, ring, cx, t0, in, WriteLds<1 - NM, 1, 2, 32>{});
-    } else {
-        acs_segment_x<0, WEIGHTED, NM>(J, ring, cx, t0, in, WriteLds<1 - NM, 1, 4, 0>{});
-    }
+    round_write<1 - NM, 1>(J, cx);
+    acs_segment<0, WEIGHTED, NM>(J, ring, cx, t0, in);
+    if constexpr (R == 2) acs_segment<1, WEIGHTED, NM>(J, ring, cx, t0, in);
     __syncthreads();
     round_read<1 - NM, 1>(J, cx);
     if constexpr (R == 1) ring_fill<32>(ring, cx.rs, cx.voff);
@@ -239,23 +238,24 @@ __device__ __forceinline__ void tail_steps(uint32_t (&J)[kRegs], float4 (&ring)[
     if constexpr (R == 2) acs_segment<3, WEIGHTED, NM>(J, ring, cx, t0, in);
 }
 
+// Register part of the state a register holds after step P of a super-step, and the
+// lane's lowest (cost, state).
+template <int P>
+struct lane_argmin_key {
+    static constexpr uint32_t of(int r) {
+        return state_of(P, 0, 0, static_cast<uint32_t>(r));
+    }
+};
 template <int P, int NM>
 __device__ __forceinline__ void lane_argmin(const uint32_t (&J)[kRegs], uint32_t w,
                                             uint32_t l, uint32_t &bv, uint32_t &bi) {
-    // the state of slot (w, l, r) is the OR of a lane/wave part and a register part
-    const uint32_t lanepart = state_of(P, w, l, 0);
-#pragma unroll
-    for (int r = 0; r < kRegs; ++r) {
-        const uint32_t s = lanepart | state_of(P, 0, 0, r);
-        const uint32_t v = J[phys(NM, r)];
-        if (v < bv || (v == bv && s < bi)) {
-            bv = v;
-            bi = s;
-        }
-    }
+    lane_best<lane_argmin_key<P>, NM>(J, state_of(P, w, l, 0), bv, bi);
 }
 
-template <bool WEIGHTED>
+// R = n mod 3, the steps after the last whole super-step: a template argument, so that
+// each instantiation has one tail (with the three tails in one kernel the compiler merged
+// their register assignments and spilled to scratch at the joins).
+template <bool WEIGHTED, int R>
 __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     const float *__restrict__ W, int64_t ldw, const float *__restrict__ d,
     const float4 *__restrict__ cb, int n, int64_t blocks_per_row, int64_t block0,
@@ -286,8 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     // one runs under naming 1 and the tail under naming 0.
 #pragma unroll
     for (int r = 0; r < kRegs; ++r) asm volatile("" : "+v"(J[r]));  // keep the zeros opaque
-    const int Q = n / 3;
-    const int R = n % 3;
+    const int Q = n / 3;  // n % 3 == R (checked by the launcher)
     StepIn in = load_steps<WEIGHTED>(cx, 0);
     if (Q & 1) {
         StepIn next;
@@ -300,9 +299,9 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
         super_step<WEIGHTED, 1>(J, ring, cx, 3 * q + 3, mid, next);
         in = next;
     }
-    if (R == 1) {
+    if constexpr (R == 1) {
         tail_steps<WEIGHTED, 0, 1>(J, ring, cx, 3 * Q, in);
-    } else if (R == 2) {
+    } else if constexpr (R == 2) {
         tail_steps<WEIGHTED, 0, 2>(J, ring, cx, 3 * Q, in);
     } else {
         round_write<1, 1>(J, cx);  // the last round (zeros if there was no super-step)
@@ -313,9 +312,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     uint32_t bv = 0xFFFFFFFFu;  // above every finite or infinite cost pattern
     uint32_t bi = 0xFFFFFFFFu;
     // final layout: step R of a super-step (R = 0: its start) under naming 0
-    if (R == 1) lane_argmin<1, 0>(J, w, l, bv, bi);
-    else if (R == 2) lane_argmin<2, 0>(J, w, l, bv, bi);
-    else lane_argmin<0, 0>(J, w, l, bv, bi);
+    lane_argmin<R, 0>(J, w, l, bv, bi);
     block_select(bv, bi, w, l, send + blockIdx.x, cost_out + blk);
 }
 
@@ -474,25 +471,19 @@ hipError_t launch_acs_l16(const Problem &p, const Plan &pl, const float *W, cons
     uint32_t *send = reinterpret_cast<uint32_t *>(per + nb * pl.bp_bytes);
     const float4 *cb = reinterpret_cast<const float4 *>(ws);
     const int64_t bp_per_block = static_cast<int64_t>(pl.bp_bytes / sizeof(uint2));
-    if (d) {
-        auto kern = acs_l16_kernel<true>;
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(kLdsBytes));
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nb)), dim3(kThreads), kLdsBytes, s,
-                           W, p.ldw, d, cb, p.n, p.blocks_per_row, block0, bp, bp_per_block,
-                           send, cost);
-    } else {
-        auto kern = acs_l16_kernel<false>;
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           static_cast<int>(kLdsBytes));
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nb)), dim3(kThreads), kLdsBytes, s,
-                           W, p.ldw, d, cb, p.n, p.blocks_per_row, block0, bp, bp_per_block,
-                           send, cost);
-    }
+    using Kern = void (*)(const float *, int64_t, const float *, const float4 *, int, int64_t,
+                          int64_t, uint2 *, int64_t, uint32_t *, float *);
+    static constexpr Kern kKernels[2][3] = {
+        {acs_l16_kernel<false, 0>, acs_l16_kernel<false, 1>, acs_l16_kernel<false, 2>},
+        {acs_l16_kernel<true, 0>, acs_l16_kernel<true, 1>, acs_l16_kernel<true, 2>}};
+    const Kern kern = kKernels[d ? 1 : 0][p.n % 3];
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(kLdsBytes));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nb)), dim3(kThreads), kLdsBytes, s, W,
+                       p.ldw, d, cb, p.n, p.blocks_per_row, block0, bp, bp_per_block, send,
+                       cost);
     return hipGetLastError();
 }
 

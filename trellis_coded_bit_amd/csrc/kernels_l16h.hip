@@ -299,36 +299,35 @@ __device__ __forceinline__ void super_step_h(uint32_t (&J)[kRegs],
 template <bool WEIGHTED, int V, int MP, int R>
 __device__ __forceinline__ void tail_h(uint32_t (&J)[kRegs], float4 (&ring)[Ring<V>::kSize],
                                        const CtxH &cx, int h0, const StepInH &in) {
-    if constexpr (R == 2) {
-        acsh_segment_x<0, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in, WriteLds<1, 1, 2, 0>{});
-        acsh_segment_x<1, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in, WriteLds<1, 1, 2, 32>{});
-    } else {
-        acsh_segment_x<0, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in, WriteLds<1, 1, 4, 0>{});
-    }
+    round_write<1, 1>(J, cx);  // round 1 of the last transposition, in one go
+    acsh_segment<0, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
+    if constexpr (R == 2) acsh_segment<1, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
     __syncthreads();
     round_read<1, 1>(J, cx);
     acsh_segment<2, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
     if constexpr (R == 2) acsh_segment<3, WEIGHTED, 0, V, MP>(J, ring, cx, h0, in);
 }
 
+// Register part of the true state (halves of every nibble swapped back) a register holds
+// after half-step P: ties between end states go to the lowest true index.
+template <int P>
+struct lane_argmin_h_key {
+    static constexpr uint32_t of(int r) {
+        return nibble_halves_swap(state_of(P, 0, 0, static_cast<uint32_t>(r)));
+    }
+};
 template <int P, int NM>
 __device__ __forceinline__ void lane_argmin_h(const uint32_t (&J)[kRegs], uint32_t w,
                                               uint32_t l, uint32_t &bv, uint32_t &bi) {
-    // ties between end states go to the lowest true index P(state)
-    const uint32_t lanepart = nibble_halves_swap(state_of(P, w, l, 0));
-#pragma unroll
-    for (int r = 0; r < kRegs; ++r) {
-        const uint32_t s = lanepart | nibble_halves_swap(state_of(P, 0, 0, r));
-        const uint32_t v = J[phys(NM, r)];
-        if (v < bv || (v == bv && s < bi)) {
-            bv = v;
-            bi = s;
-        }
-    }
+    lane_best<lane_argmin_h_key<P>, NM>(J, nibble_halves_swap(state_of(P, w, l, 0)), bv, bi);
 }
 
 // n = full steps per block; the kernel runs 2n half-steps.
-template <bool WEIGHTED, int V>
+// R = 2n mod 3, the half-steps after the last whole super-step, and QP = (2n / 3) mod 2,
+// the pattern of the last super-step, are template arguments, so that each instantiation
+// has one loop and one tail (with both chosen at run time the compiler merged their
+// register assignments and spilled to scratch at the joins).
+template <bool WEIGHTED, int V, int R, int QP>
 __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
     const float *__restrict__ W, int64_t ldw, const float *__restrict__ d,
     const float4 *__restrict__ cb, int n, int64_t blocks_per_row, int64_t block0,
@@ -357,10 +356,9 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
     // tail) writes out as it goes
 
     const int nh = 2 * n;
-    const int Q = nh / 3;
-    const int R = nh % 3;
+    const int Q = nh / 3;  // nh % 3 == R and Q % 2 == QP (chosen by the launcher)
     StepInH in = load_h<WEIGHTED, V>(cx, 0);
-    if (Q & 1) {
+    if constexpr (QP == 1) {
         StepInH next;
         super_step_h<WEIGHTED, 1, V, 0>(J, ring, cx, 0, in, next);
         in = next;
@@ -379,12 +377,10 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
         }
     }
     // the tail is super-step Q, pattern Q mod 2
-    if (R == 1) {
-        if (Q & 1) tail_h<WEIGHTED, V, 1, 1>(J, ring, cx, 3 * Q, in);
-        else tail_h<WEIGHTED, V, 0, 1>(J, ring, cx, 3 * Q, in);
-    } else if (R == 2) {
-        if (Q & 1) tail_h<WEIGHTED, V, 1, 2>(J, ring, cx, 3 * Q, in);
-        else tail_h<WEIGHTED, V, 0, 2>(J, ring, cx, 3 * Q, in);
+    if constexpr (R == 1) {
+        tail_h<WEIGHTED, V, QP, 1>(J, ring, cx, 3 * Q, in);
+    } else if constexpr (R == 2) {
+        tail_h<WEIGHTED, V, QP, 2>(J, ring, cx, 3 * Q, in);
     } else {
         round_write<1, 1>(J, cx);
         __syncthreads();
@@ -393,9 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
 
     uint32_t bv = 0xFFFFFFFFu;
     uint32_t bi = 0xFFFFFFFFu;
-    if (R == 1) lane_argmin_h<1, 0>(J, w, l, bv, bi);
-    else if (R == 2) lane_argmin_h<2, 0>(J, w, l, bv, bi);
-    else lane_argmin_h<0, 0>(J, w, l, bv, bi);
+    lane_argmin_h<R, 0>(J, w, l, bv, bi);
     block_select(bv, bi, w, l, send + blockIdx.x, cost_out + blk);
 }
 
@@ -405,7 +399,13 @@ template <bool WEIGHTED, int V>
 hipError_t launch_h(const Problem &p, int64_t block0, int64_t nb, const float *W,
                     const float *d, const float4 *cb, uint2 *bp, int64_t bp_per_block,
                     uint32_t *send, float *cost, hipStream_t s) {
-    auto kern = acs_l16h_kernel<WEIGHTED, V>;
+    using Kern = void (*)(const float *, int64_t, const float *, const float4 *, int, int64_t,
+                          int64_t, uint2 *, int64_t, uint32_t *, float *);
+    static constexpr Kern kKernels[3][2] = {
+        {acs_l16h_kernel<WEIGHTED, V, 0, 0>, acs_l16h_kernel<WEIGHTED, V, 0, 1>},
+        {acs_l16h_kernel<WEIGHTED, V, 1, 0>, acs_l16h_kernel<WEIGHTED, V, 1, 1>},
+        {acs_l16h_kernel<WEIGHTED, V, 2, 0>, acs_l16h_kernel<WEIGHTED, V, 2, 1>}};
+    const Kern kern = kKernels[(2 * p.n) % 3][((2 * p.n) / 3) % 2];
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(kLdsBytes));

@@ -240,22 +240,23 @@ __device__ __forceinline__ void super_step3(uint32_t (&J)[kRegs], float4 (&ring)
     __syncthreads();  // every wave has read round 0
 }
 
+// Register part of the state a register holds after step P of a 3-bit super-step, and the
+// lane's lowest (cost, state).
+template <int P>
+struct lane_argmin3_key {
+    static constexpr uint32_t of(int r) {
+        return state_of3(P, 0, 0, static_cast<uint32_t>(r));
+    }
+};
 template <int P, int NM>
 __device__ __forceinline__ void lane_argmin3(const uint32_t (&J)[kRegs], uint32_t w,
                                              uint32_t l, uint32_t &bv, uint32_t &bi) {
-    const uint32_t lanepart = state_of3(P, w, l, 0);
-#pragma unroll
-    for (int r = 0; r < kRegs; ++r) {
-        const uint32_t s = lanepart | state_of3(P, 0, 0, r);
-        const uint32_t v = J[phys(NM, r)];
-        if (v < bv || (v == bv && s < bi)) {
-            bv = v;
-            bi = s;
-        }
-    }
+    lane_best<lane_argmin3_key<P>, NM>(J, state_of3(P, w, l, 0), bv, bi);
 }
 
-template <bool WEIGHTED>
+// R = n mod 2 (one step after the last whole super-step, or none): a template argument,
+// so that each instantiation has one tail and no merged register assignment.
+template <bool WEIGHTED, int R>
 __global__ __launch_bounds__(kThreads, 1) void acs_l16k3_kernel(
     const float *__restrict__ W, int64_t ldw, const float *__restrict__ d,
     const float4 *__restrict__ cb, int n, int64_t blocks_per_row, int64_t block0,
@@ -280,8 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16k3_kernel(
     // the all-zero start is round 1 of a transposition that the first super-step (or the
     // tail) writes out as it goes
 
-    const int Q = n / 2;
-    const int R = n % 2;
+    const int Q = n / 2;  // n % 2 == R (checked by the launcher)
     StepIn in = load_steps<WEIGHTED>(cx, 0);
     if (Q & 1) {
         StepIn next;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16k3_kernel(
         super_step3<WEIGHTED, 1>(J, ring, cx, 2 * q + 2, mid, next);
         in = next;
     }
-    if (R == 1) {  // one more step: segments 0 and 1 under naming 0
+    if constexpr (R == 1) {  // one more step: segments 0 and 1 under naming 0
         acs3_segment_x<0, WEIGHTED, 0>(J, ring, cx, 2 * Q, in, WriteLds<1, 1, 8, 0>{});
         __syncthreads();
         round_read<1, 1>(J, cx);
@@ -307,10 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16k3_kernel(
 
     uint32_t bv = 0xFFFFFFFFu;
     uint32_t bi = 0xFFFFFFFFu;
-    if (R == 1)
-        lane_argmin3<1, 0>(J, w, l, bv, bi);
-    else
-        lane_argmin3<0, 0>(J, w, l, bv, bi);
+    lane_argmin3<R, 0>(J, w, l, bv, bi);
     block_select(bv, bi, w, l, send + blockIdx.x, cost_out + blk);
 }
 
@@ -404,7 +401,11 @@ hipError_t launch_acs_l16k3(const Problem &p, const Plan &pl, const float *W, co
     uint32_t *send = reinterpret_cast<uint32_t *>(per + nb * pl.bp_bytes);
     const float4 *cb = reinterpret_cast<const float4 *>(ws);
     const int64_t bp_per_block = static_cast<int64_t>(pl.bp_bytes / sizeof(uint2));
-    auto kern = d ? acs_l16k3_kernel<true> : acs_l16k3_kernel<false>;
+    using Kern = void (*)(const float *, int64_t, const float *, const float4 *, int, int64_t,
+                          int64_t, uint2 *, int64_t, uint32_t *, float *);
+    static constexpr Kern kKernels[2][2] = {{acs_l16k3_kernel<false, 0>, acs_l16k3_kernel<false, 1>},
+                                            {acs_l16k3_kernel<true, 0>, acs_l16k3_kernel<true, 1>}};
+    const Kern kern = kKernels[d ? 1 : 0][p.n % 2];
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(kLdsBytes));

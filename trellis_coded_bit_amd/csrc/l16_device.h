@@ -235,6 +235,45 @@ struct ReadLds {
     }
 };
 
+// The lane's registers in ascending order of Key::of(r), the register part of the state a
+// register holds (the lane part is common to all of them and occupies other bits, so this
+// is also the order of the full states).
+template <class Key>
+struct AscendingRegs {
+    int r[kRegs];
+    constexpr AscendingRegs() : r{} {
+        for (int i = 0; i < kRegs; ++i) r[i] = i;
+        for (int i = 1; i < kRegs; ++i)
+            for (int j = i; j > 0 && Key::of(r[j]) < Key::of(r[j - 1]); --j) {
+                const int t = r[j];
+                r[j] = r[j - 1];
+                r[j - 1] = t;
+            }
+    }
+};
+template <class Key, int NM, int... K>
+__device__ __forceinline__ void lane_best_impl(const uint32_t (&J)[kRegs], uint32_t &bv,
+                                               uint32_t &bs, std::integer_sequence<int, K...>) {
+    constexpr AscendingRegs<Key> ord{};
+    // strict '<' in ascending state order keeps the lowest state among equal costs; every
+    // cost pattern is below 0xFFFFFFFF (costs are never negative), so the first register
+    // always replaces the start value
+    ((bs = J[phys(NM, ord.r[K])] < bv ? Key::of(ord.r[K]) : bs,
+      bv = J[phys(NM, ord.r[K])] < bv ? J[phys(NM, ord.r[K])] : bv),
+     ...);
+}
+// The lane's smallest cost pattern bv and, among its registers of that cost, the lowest
+// state lanepart | Key::of(r), in branch-free selects (the branchy form of this loop left
+// the compiler short of registers and spilling in the kernels' last lines).
+template <class Key, int NM>
+__device__ __forceinline__ void lane_best(const uint32_t (&J)[kRegs], uint32_t lanepart,
+                                          uint32_t &bv, uint32_t &bi) {
+    uint32_t v = 0xFFFFFFFFu, s = 0u;
+    lane_best_impl<Key, NM>(J, v, s, std::make_integer_sequence<int, kRegs>{});
+    bv = v;
+    bi = lanepart | s;
+}
+
 // Lowest-index minimum over the workgroup: (bv, bi) are each lane's best cost pattern
 // and state; lane 0 of wave 0 writes the chosen end state and its cost.
 __device__ __forceinline__ void block_select(uint32_t bv, uint32_t bi, uint32_t w, uint32_t l,
