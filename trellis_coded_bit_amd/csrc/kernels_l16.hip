@@ -222,9 +222,7 @@ __device__ __forceinline__ void super_step(uint32_t (&J)[kRegs], float4 (&ring)[
 
 // The last R = 1 or 2 steps (segments 0..3 in order; for one step the ring is refilled
 // where the order departs from a full super-step), under naming NM.  Round 1 of the last
-// transposition (naming 1 - NM) is written first, in one go: spread over the tail's
-// segments it left the compiler short of registers there (spills to scratch, once per
-// block, about 2 GB of extra HBM traffic per launch at 2048 x 2048).
+// transposition (naming 1 - NM) is written first, in one go (this runs once per block).
 template <bool WEIGHTED, int NM, int R>
 __device__ __forceinline__ void tail_steps(uint32_t (&J)[kRegs], float4 (&ring)[kRing<WEIGHTED>],
                                            const CtxL &cx, int t0, const StepIn &in) {

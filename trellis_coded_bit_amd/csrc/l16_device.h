@@ -1,6 +1,7 @@
-// Device helpers shared by the L = 16 forward kernels (k*V = 2 and 3): the per-block
-// context, the carry shift-in of compare masks, and the two LDS rounds of the
-// transposition (layout in l16_layout.h).
+// Device helpers shared by the L = 16 forward kernels (k*V = 2, 3 and 4): the per-block
+// context, the carry shift-in of compare masks, the two LDS rounds of the transposition
+// (layout in l16_layout.h) and their parts spread over a segment's groups, and the
+// lane's lowest (cost, state) at the end.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -202,10 +203,6 @@ __device__ __forceinline__ void round_read(uint32_t (&J)[kRegs], const Ctx &cx) 
 // while the VALU computes instead of in one burst behind a barrier (every wave reaches
 // the burst at the same time, and a wave issues nothing else until its LDS queue has
 // taken the whole burst).  After group I of the segment, `step<I>` issues its share.
-struct NoLds {
-    template <int I>
-    __device__ __forceinline__ void step(uint32_t (&)[kRegs], const Ctx &) const {}
-};
 // Round RHO of naming NM written PER registers per group, from register I0 + PER * I of
 // the round (pairs of consecutive registers share one ds_write2).
 template <int NM, int RHO, int PER, int I0>
