@@ -248,26 +248,63 @@ __device__ __forceinline__ void acsh_segment_x(uint32_t (&J)[kRegs],
                                                   x, std::make_integer_sequence<int, 16>{});
 }
 
-// Segment 2 (step 1 of the odd groups) with round 1 of the transposition read into the
-// registers it consumes, the four values of group i + 3 requested before group i (at
-// most 16 reads in flight; the LDS wait counter counts at most 15).
-template <bool WEIGHTED, int NM, int V, int MP, int I>
-__device__ __forceinline__ void seg2_group_h(uint32_t (&J)[kRegs],
-                                             float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
-                                             const StepInH &in, uint32_t &acc) {
-    if constexpr (I + 3 < 16) round_read_group<1 - NM, 1, I + 3>(J, cx);
-    acsh_group<2, WEIGHTED, NM, V, MP, I>(J, ring, cx, in, acc);
+// Segments SA (half-step 1) and SA + 1 (half-step 2) of one half of the groups (SA = 0:
+// even groups, SA = 2: odd), interleaved.  One of the two carries the metric, the other
+// only the minimum: the plain groups' compare -> SALU -> carry-in chains overlap the
+// metric groups' arithmetic instead of running back to back.  Step-2 group j reads the
+// registers that the step-1 groups C + 4b + 16 r[6] wrote (b = 0..3, C = its two low
+// register bits): for j < 8 those are step-1 groups 0..7, for j >= 8 groups 8..15.  So:
+// step-1 groups 0..7; then step-2 group j and step-1 group 8 + j in turn, j = 0..7; then
+// step-2 groups 8..15.  Each segment keeps its own group order, so the codebook ring and
+// the backpointer words are as in the segment-by-segment order.  READS: round 1 of the
+// transposition is read into the step-1 groups three groups ahead (the odd half), the
+// first three before the call.  X issues its LDS work after each of the 32 groups.
+template <int SA, bool WEIGHTED, int NM, int V, int MP, bool READS, int I>
+__device__ __forceinline__ void pair_step1(uint32_t (&J)[kRegs], float4 (&ring)[Ring<V>::kSize],
+                                           const CtxH &cx, const StepInH &in, uint32_t &acc) {
+    if constexpr (READS && I + 3 < 16) round_read_group<1 - NM, 1, I + 3>(J, cx);
+    acsh_group<SA, WEIGHTED, NM, V, MP, I>(J, ring, cx, in, acc);
 }
-template <bool WEIGHTED, int NM, int V, int MP, int... I>
-__device__ __forceinline__ void seg2_reading_h(uint32_t (&J)[kRegs],
+template <int SA, bool WEIGHTED, int NM, int V, int MP, bool READS, int K, class X>
+__device__ __forceinline__ void pair_slot(uint32_t (&J)[kRegs], float4 (&ring)[Ring<V>::kSize],
+                                          const CtxH &cx, const StepInH &in, uint32_t &acc1,
+                                          uint32_t &acc2, const X &x) {
+    if constexpr (K < 8) {
+        pair_step1<SA, WEIGHTED, NM, V, MP, READS, K>(J, ring, cx, in, acc1);
+    } else if constexpr (K < 24) {
+        constexpr int j = (K - 8) / 2;
+        if constexpr ((K - 8) % 2 == 0)
+            acsh_group<SA + 1, WEIGHTED, NM, V, MP, j>(J, ring, cx, in, acc2);
+        else
+            pair_step1<SA, WEIGHTED, NM, V, MP, READS, 8 + j>(J, ring, cx, in, acc1);
+    } else {
+        acsh_group<SA + 1, WEIGHTED, NM, V, MP, K - 16>(J, ring, cx, in, acc2);
+    }
+    x.template step<K>(J, cx);
+}
+template <int SA, bool WEIGHTED, int NM, int V, int MP, bool READS, class X, int... K>
+__device__ __forceinline__ void acsh_pair_impl(uint32_t (&J)[kRegs],
                                                float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
-                                               int h0, const StepInH &in,
-                                               std::integer_sequence<int, I...>) {
-    round_read_groups<1 - NM, 1>(J, cx, std::make_integer_sequence<int, 3>{});
-    uint32_t acc = 0;
-    (seg2_group_h<WEIGHTED, NM, V, MP, I>(J, ring, cx, in, acc), ...);
-    cx.bpb.store(2 * kThreads * h0 + seg_half(2), acc);
+                                               int h0, const StepInH &in, const X &x,
+                                               std::integer_sequence<int, K...>) {
+    if constexpr (READS) round_read_groups<1 - NM, 1>(J, cx, std::make_integer_sequence<int, 3>{});
+    uint32_t acc1 = 0, acc2 = 0;
+    (pair_slot<SA, WEIGHTED, NM, V, MP, READS, K>(J, ring, cx, in, acc1, acc2, x), ...);
+    cx.bpb.store(2 * kThreads * h0 + seg_half(SA), acc1);
+    cx.bpb.store(2 * kThreads * (h0 + 1) + seg_half(SA + 1), acc2);
 }
+template <int SA, bool WEIGHTED, int NM, int V, int MP, bool READS, class X>
+__device__ __forceinline__ void acsh_pair(uint32_t (&J)[kRegs], float4 (&ring)[Ring<V>::kSize],
+                                          const CtxH &cx, int h0, const StepInH &in,
+                                          const X &x) {
+    acsh_pair_impl<SA, WEIGHTED, NM, V, MP, READS>(J, ring, cx, h0, in, x,
+                                                   std::make_integer_sequence<int, 32>{});
+}
+// No LDS work between the groups.
+struct NoLds {
+    template <int I>
+    __device__ __forceinline__ void step(uint32_t (&)[kRegs], const Ctx &) const {}
+};
 
 // Super-step under naming NM and pattern MP, with the weights of its half-steps in `in`
 // and those of the next super-step requested into `next`; the transposition rounds are
@@ -278,12 +315,9 @@ template <bool WEIGHTED, int NM, int V, int MP>
 __device__ __forceinline__ void super_step_h(uint32_t (&J)[kRegs],
                                              float4 (&ring)[Ring<V>::kSize], const CtxH &cx,
                                              int h0, const StepInH &in, StepInH &next) {
-    acsh_segment_x<0, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in, WriteLds<1 - NM, 1, 2, 0>{});
-    acsh_segment_x<1, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in, WriteLds<1 - NM, 1, 2, 32>{});
+    acsh_pair<0, WEIGHTED, NM, V, MP, false>(J, ring, cx, h0, in, WriteLds<1 - NM, 1, 2, 0>{});
     __syncthreads();  // round-1 values written by every wave
-    seg2_reading_h<WEIGHTED, NM, V, MP>(J, ring, cx, h0, in,
-                                        std::make_integer_sequence<int, 16>{});
-    acsh_segment<3, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in);
+    acsh_pair<2, WEIGHTED, NM, V, MP, true>(J, ring, cx, h0, in, NoLds{});
     __syncthreads();  // every wave has read round 1
     acsh_segment_x<4, WEIGHTED, NM, V, MP>(J, ring, cx, h0, in, WriteRound0Lagged<NM, 4>{});
     round_write_range<NM, 0, 60, 4>(J, cx);
