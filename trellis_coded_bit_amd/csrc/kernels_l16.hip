@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16_kernel(
     // one runs under naming 1 and the tail under naming 0.
 #pragma unroll
     for (int r = 0; r < kRegs; ++r) asm volatile("" : "+v"(J[r]));  // keep the zeros opaque
-    const int Q = n / 3;  // n % 3 == R (checked by the launcher)
+    const int Q = n / 3;  // n % 3 == R: the launcher picks the instantiation
     StepIn in = load_steps<WEIGHTED>(cx, 0);
     if (Q & 1) {
         StepIn next;

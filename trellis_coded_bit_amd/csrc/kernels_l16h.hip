@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
     // tail) writes out as it goes
 
     const int nh = 2 * n;
-    const int Q = nh / 3;  // nh % 3 == R and Q % 2 == QP (chosen by the launcher)
+    const int Q = nh / 3;  // nh % 3 == R, Q % 2 == QP: the launcher picks the instantiation
     StepInH in = load_h<WEIGHTED, V>(cx, 0);
     if constexpr (QP == 1) {
         StepInH next;

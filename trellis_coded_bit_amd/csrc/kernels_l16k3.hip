@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16k3_kernel(
     // the all-zero start is round 1 of a transposition that the first super-step (or the
     // tail) writes out as it goes
 
-    const int Q = n / 2;  // n % 2 == R (checked by the launcher)
+    const int Q = n / 2;  // n % 2 == R: the launcher picks the instantiation
     StepIn in = load_steps<WEIGHTED>(cx, 0);
     if (Q & 1) {
         StepIn next;
