@@ -12,12 +12,16 @@
 //  - the k*V = 4 half-step patterns place the metric on the even half-steps and list
 //    every metric group once, in processing order;
 //  - the k*V = 4 relabelling of the state commutes with the shift and makes the two
-//    half-step minima pick the lowest predecessor index.
+//    half-step minima pick the lowest predecessor index;
+//  - the transposition rounds spread over the segments touch no register the segment
+//    they run in uses, refill exactly the registers they freed, and the k*V = 4
+//    kernel's interleaved segment pairs respect every register dependency.
 #define __host__
 #define __device__
 #include <cstdio>
 #include <cstdlib>
 #include <set>
+#include <utility>
 #include <vector>
 
 #include "l16_layout.h"
@@ -32,6 +36,107 @@ static int fails = 0;
             ++fails;                                                     \
         }                                                                \
     } while (0)
+
+
+// Registers (physical, one lane) of a group of 2-bit step p and of 3-bit step p under
+// naming nm.
+static std::set<uint32_t> group_regs2(int nm, int p, uint32_t g) {
+    std::set<uint32_t> out;
+    for (uint32_t b = 0; b < 4; ++b) out.insert(phys(nm, group_reg(p, g, b)));
+    return out;
+}
+static std::set<uint32_t> group_regs3(int nm, int p, uint32_t g) {
+    std::set<uint32_t> out;
+    for (uint32_t b = 0; b < 8; ++b) out.insert(phys(nm, group_reg3(p, g, b)));
+    return out;
+}
+static bool disjoint(const std::set<uint32_t> &a, const std::set<uint32_t> &b) {
+    for (uint32_t x : a)
+        if (b.count(x)) return false;
+    return true;
+}
+
+// The transposition rounds spread over the segments (kernels_l16*.hip, l16_device.h):
+// the registers a round writes out while a segment runs are not touched by that
+// segment's groups, the registers a round reads back are exactly those it freed, and in
+// the k*V = 4 kernel's interleaved segment pairs every step-2 group comes after the
+// step-1 groups whose registers it reads, with no later step-1 group writing them.
+static void check_spread_rounds() {
+    for (int nm = 0; nm < 2; ++nm) {
+        // round 1 of the previous transposition: logical r[6] = 1 of naming 1 - nm
+        std::set<uint32_t> r1w, r0w, r1r, r0r;
+        for (uint32_t i = 0; i < 64; ++i) r1w.insert(phys(1 - nm, 64 + i));
+        for (uint32_t i = 0; i < 64; ++i) r0w.insert(phys(nm, i));
+        for (uint32_t g2 = 0; g2 < 16; ++g2)
+            for (uint32_t b = 0; b < 4; ++b) {
+                // round_read_group<1 - nm, 1, g2> and <nm, 0, g2> targets
+                r1r.insert(phys(nm, group_reg(1, 2 * g2 + 1, b)));
+                r0r.insert(phys(1 - nm, group_reg(1, 2 * g2, b)));
+            }
+        CHECK(r1w == r1r);  // round 1 refills exactly the registers it wrote out
+        CHECK(r0w == r0r);  // so does round 0
+        // k*V = 2 and 4: segments 0-1 (steps 1-2, even groups) while round 1 is written;
+        // segment 2 (step 1, odd groups) refills round 1
+        for (int seg = 0; seg < 2; ++seg)
+            for (int i = 0; i < 16; ++i)
+                CHECK(disjoint(group_regs2(nm, seg_step(seg), seg_group(seg, i)), r1w));
+        // segment 4 (step 3, groups 0..15) writes round 0 one group behind: group I's
+        // registers are logical 4I .. 4I + 3, and no later group of segments 4-5 uses them
+        for (uint32_t g = 0; g < 16; ++g) {
+            std::set<uint32_t> own;
+            for (uint32_t b = 0; b < 4; ++b) own.insert(phys(nm, 4 * g + b));
+            CHECK(own == group_regs2(nm, 3, seg_group(4, g)));
+            for (uint32_t h = g + 1; h < 32; ++h)
+                CHECK(disjoint(own, group_regs2(nm, 3, h)));
+        }
+        // segment 5 (step 3, groups 16..31) while round 0 is read back
+        for (int i = 0; i < 16; ++i)
+            CHECK(disjoint(group_regs2(nm, 3, seg_group(5, i)), r0r));
+        // k*V = 3: segment 0 (step 1, even groups) while round 1 is written; segment 2
+        // (step 2, groups 0..7) writes round 0 one group behind (group g = registers
+        // 8g .. 8g + 7); segment 3 (groups 8..15) while round 0 is read back
+        for (int i = 0; i < 8; ++i) {
+            CHECK(disjoint(group_regs3(nm, 1, seg3_group(0, i)), r1w));
+            std::set<uint32_t> own;
+            for (uint32_t b = 0; b < 8; ++b) own.insert(phys(nm, 8 * i + b));
+            CHECK(own == group_regs3(nm, 2, seg3_group(2, i)));
+            CHECK(disjoint(group_regs3(nm, 2, seg3_group(3, i)), r0r));
+        }
+        std::set<uint32_t> r1r3;
+        for (int i = 0; i < 8; ++i)
+            for (uint32_t b = 0; b < 8; ++b) r1r3.insert(phys(nm, group_reg3(1, seg3_group(1, i), b)));
+        CHECK(r1r3 == r1w);
+        // k*V = 4 segment pairs (SA = 0: even groups, 2: odd): order of the 32 groups
+        for (int sa = 0; sa <= 2; sa += 2) {
+            std::vector<std::pair<int, int>> order;  // (step, index within its segment)
+            for (int k = 0; k < 32; ++k) order.push_back({pair_step(k), pair_index(k)});
+            std::vector<int> pos1(16, -1), pos2(16, -1);
+            for (int k = 0; k < 32; ++k) (order[k].first == 1 ? pos1 : pos2)[order[k].second] = k;
+            for (int i = 0; i < 16; ++i) CHECK(pos1[i] >= 0 && pos2[i] >= 0);
+            for (int i = 1; i < 16; ++i) CHECK(pos1[i] > pos1[i - 1] && pos2[i] > pos2[i - 1]);
+            for (int j = 0; j < 16; ++j) {
+                const auto rd = group_regs2(nm, 2, seg_group(sa + 1, j));
+                for (int i = 0; i < 16; ++i) {
+                    const auto wr = group_regs2(nm, 1, seg_group(sa, i));
+                    // a step-1 group sharing registers with step-2 group j comes first
+                    if (!disjoint(rd, wr)) CHECK(pos1[i] < pos2[j]);
+                }
+            }
+            if (sa == 2) {
+                // round 1 is read into step-1 group i + 3 before step-1 group i: no group
+                // placed between the read and step-1 group i + 3 touches its registers
+                for (int i = 0; i + 3 < 16; ++i) {
+                    const auto tgt = group_regs2(nm, 1, seg_group(sa, i + 3));
+                    for (int k = pos1[i]; k < pos1[i + 3]; ++k) {
+                        const auto &o = order[k];
+                        const auto regs = group_regs2(nm, o.first, seg_group(sa + o.first - 1, o.second));
+                        CHECK(disjoint(regs, tgt));
+                    }
+                }
+            }
+        }
+    }
+}
 
 int main() {
     // bijection and inverse
@@ -267,6 +372,7 @@ int main() {
         }
         check_two_stage(c);
     }
+    check_spread_rounds();
     if (fails) {
         std::printf("%d failures\n", fails);
         return 1;

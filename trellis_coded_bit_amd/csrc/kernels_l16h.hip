@@ -249,14 +249,12 @@ __device__ __forceinline__ void acsh_segment_x(uint32_t (&J)[kRegs],
 }
 
 // Segments SA (half-step 1) and SA + 1 (half-step 2) of one half of the groups (SA = 0:
-// even groups, SA = 2: odd), interleaved.  One of the two carries the metric, the other
-// only the minimum: the plain groups' compare -> SALU -> carry-in chains overlap the
-// metric groups' arithmetic instead of running back to back.  Step-2 group j reads the
-// registers that the step-1 groups C + 4b + 16 r[6] wrote (b = 0..3, C = its two low
-// register bits): for j < 8 those are step-1 groups 0..7, for j >= 8 groups 8..15.  So:
-// step-1 groups 0..7; then step-2 group j and step-1 group 8 + j in turn, j = 0..7; then
-// step-2 groups 8..15.  Each segment keeps its own group order, so the codebook ring and
-// the backpointer words are as in the segment-by-segment order.  READS: round 1 of the
+// even groups, SA = 2: odd), interleaved in the order pair_step / pair_index of
+// l16_layout.h (every step-2 group after the step-1 groups it reads).  One of the two
+// carries the metric, the other only the minimum: the plain groups' compare -> SALU ->
+// carry-in chains overlap the metric groups' arithmetic instead of running back to
+// back.  Each segment keeps its own group order, so the codebook ring and the
+// backpointer words are as in the segment-by-segment order.  READS: round 1 of the
 // transposition is read into the step-1 groups three groups ahead (the odd half), the
 // first three before the call.  X issues its LDS work after each of the 32 groups.
 template <int SA, bool WEIGHTED, int NM, int V, int MP, bool READS, int I>
@@ -269,17 +267,11 @@ template <int SA, bool WEIGHTED, int NM, int V, int MP, bool READS, int K, class
 __device__ __forceinline__ void pair_slot(uint32_t (&J)[kRegs], float4 (&ring)[Ring<V>::kSize],
                                           const CtxH &cx, const StepInH &in, uint32_t &acc1,
                                           uint32_t &acc2, const X &x) {
-    if constexpr (K < 8) {
-        pair_step1<SA, WEIGHTED, NM, V, MP, READS, K>(J, ring, cx, in, acc1);
-    } else if constexpr (K < 24) {
-        constexpr int j = (K - 8) / 2;
-        if constexpr ((K - 8) % 2 == 0)
-            acsh_group<SA + 1, WEIGHTED, NM, V, MP, j>(J, ring, cx, in, acc2);
-        else
-            pair_step1<SA, WEIGHTED, NM, V, MP, READS, 8 + j>(J, ring, cx, in, acc1);
-    } else {
-        acsh_group<SA + 1, WEIGHTED, NM, V, MP, K - 16>(J, ring, cx, in, acc2);
-    }
+    constexpr int I = pair_index(K);
+    if constexpr (pair_step(K) == 1)
+        pair_step1<SA, WEIGHTED, NM, V, MP, READS, I>(J, ring, cx, in, acc1);
+    else
+        acsh_group<SA + 1, WEIGHTED, NM, V, MP, I>(J, ring, cx, in, acc2);
     x.template step<K>(J, cx);
 }
 template <int SA, bool WEIGHTED, int NM, int V, int MP, bool READS, class X, int... K>

@@ -196,6 +196,20 @@ __host__ __device__ constexpr int metric_index(int mp, int seg) {
 }
 
 
+// k*V = 4: a step-1 segment and the step-2 segment after it (segments 0-1 or 2-3, one
+// of them a plain half-step) are processed as one interleaved sequence of 32 groups.
+// Step-2 group j reads the registers that step-1 groups C + 4b + 16 r[6] wrote (C its
+// two low register bits), i.e. groups 0..7 for j < 8 and 8..15 for j >= 8, so: step-1
+// groups 0..7; then step-2 group j and step-1 group 8 + j in turn (j = 0..7); then
+// step-2 groups 8..15.  Slot k (0..31) holds the group pair_index(k) of half-step
+// pair_step(k) (1 or 2).
+__host__ __device__ constexpr int pair_step(int k) {
+    return k < 8 ? 1 : (k < 24 ? ((k - 8) % 2 == 0 ? 2 : 1) : 2);
+}
+__host__ __device__ constexpr int pair_index(int k) {
+    return k < 8 ? k : (k < 24 ? ((k - 8) % 2 == 0 ? (k - 8) / 2 : 8 + (k - 8) / 2) : k - 16);
+}
+
 // Register naming.  Odd super-steps keep logical register r in physical register
 // phys(1, r) = r with bits 0 and 6 swapped.  A transposition round then refills exactly
 // the physical registers it has just written out: round 0 moves logical r[6] = 0 into
