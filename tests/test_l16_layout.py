@@ -1,5 +1,6 @@
 """Host check of the L = 16 kernel's index math (slot <-> state bijections, group
-structure, the three-step transposition, LDS staging addresses and bank spread).
+structure, the three-step transposition, LDS staging addresses and bank spread, the
+transposition rounds spread over the segments, and the k*V = 4 segment-pair order).
 Compiles tests/l16_layout_check.cpp against the kernel's own layout header with g++
 and runs it on the CPU."""
 import os
