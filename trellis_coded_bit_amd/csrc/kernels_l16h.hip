@@ -349,11 +349,12 @@ __device__ __forceinline__ void lane_argmin_h(const uint32_t (&J)[kRegs], uint32
 }
 
 // n = full steps per block; the kernel runs 2n half-steps.
-// R = 2n mod 3, the half-steps after the last whole super-step, and QP = (2n / 3) mod 2,
-// the pattern of the last super-step, are template arguments, so that each instantiation
-// has one loop and one tail (with both chosen at run time the compiler merged their
-// register assignments and spilled to scratch at the joins).
-template <bool WEIGHTED, int V, int R, int QP>
+// R = 2n mod 3, the half-steps after the last whole super-step, is a template argument,
+// so that each instantiation has one loop and one tail (with the tails chosen at run
+// time the compiler merged their register assignments and spilled to scratch at the
+// joins).  It also fixes the pattern QP = Q mod 2 of the last whole super-step: 2n = 3Q
+// + R is even, so Q and R have the same parity.
+template <bool WEIGHTED, int V, int R>
 __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
     const float *__restrict__ W, int64_t ldw, const float *__restrict__ d,
     const float4 *__restrict__ cb, int n, int64_t blocks_per_row, int64_t block0,
@@ -382,7 +383,8 @@ __global__ __launch_bounds__(kThreads, 1) void acs_l16h_kernel(
     // tail) writes out as it goes
 
     const int nh = 2 * n;
-    const int Q = nh / 3;  // nh % 3 == R, Q % 2 == QP: the launcher picks the instantiation
+    const int Q = nh / 3;  // nh % 3 == R: the launcher picks the instantiation
+    constexpr int QP = R % 2;  // == Q % 2
     StepInH in = load_h<WEIGHTED, V>(cx, 0);
     if constexpr (QP == 1) {
         StepInH next;
@@ -427,11 +429,10 @@ hipError_t launch_h(const Problem &p, int64_t block0, int64_t nb, const float *W
                     uint32_t *send, float *cost, hipStream_t s) {
     using Kern = void (*)(const float *, int64_t, const float *, const float4 *, int, int64_t,
                           int64_t, uint2 *, int64_t, uint32_t *, float *);
-    static constexpr Kern kKernels[3][2] = {
-        {acs_l16h_kernel<WEIGHTED, V, 0, 0>, acs_l16h_kernel<WEIGHTED, V, 0, 1>},
-        {acs_l16h_kernel<WEIGHTED, V, 1, 0>, acs_l16h_kernel<WEIGHTED, V, 1, 1>},
-        {acs_l16h_kernel<WEIGHTED, V, 2, 0>, acs_l16h_kernel<WEIGHTED, V, 2, 1>}};
-    const Kern kern = kKernels[(2 * p.n) % 3][((2 * p.n) / 3) % 2];
+    static constexpr Kern kKernels[3] = {acs_l16h_kernel<WEIGHTED, V, 0>,
+                                         acs_l16h_kernel<WEIGHTED, V, 1>,
+                                         acs_l16h_kernel<WEIGHTED, V, 2>};
+    const Kern kern = kKernels[(2 * p.n) % 3];
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(kLdsBytes));
